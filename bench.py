@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the ZeRO-3 shard step on one MI355X.
+
+Workload (default): rank 0's shard of a LLaMA-70B-shaped model at D = 8
+simulated ranks -- 80 decoder-block units (d = 8192, GQA k/v 1024 wide,
+FFN 28672) plus the root unit (embedding, final norm, LM head), one bucket
+per unit: 81 buckets, 8,622,081,024 shard parameters with fp32 master, m
+and v (103.5 GB) and a bf16 working shard (17.2 GB), all resident in HBM.
+
+One step = for each unit, in order:
+  1. zs_adamw_step: the fused reduce-scatter arithmetic + AdamW on the
+     unit's shard, from 8 bf16 gradient contributions (what the
+     reduce-scatter delivers; a pool of 4 distinct contribution sets is
+     cycled over the buckets, generated before timing);
+  2. zs_gather_unit: the all-gather's local rebuild of the unit's full bf16
+     parameters (855.7M for a block) into the transient unit buffer, from
+     this rank's fresh shard and the 7 peer shards.
+The flat layout and pack of a unit happen once, at wrap time; they are
+timed separately (one block unit, fp32) and reported under "wrap".
+
+Prints one JSON line. `value` is shard params/s over the whole step;
+`roofline` is the fused AdamW kernel's achieved HBM bandwidth from HIP
+events on its stream; `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload (one full block bucket, one step).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "params/s and achieved HBM GB/s (% of peak) for fused reduce+AdamW shard step"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+CONTRIB_POOL = 4
+PMC_FILE = os.path.join(ROOT, "profiles", "adamw_fused_llama70b_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "fsdp_sharded_optimizer_zs_amd", "csrc", "zs_step.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(bytes_per_launch_alg: float):
+    """Measured HBM bytes per launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(PMC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_src_sha256_16") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(p, m, v, contribs, t: int, hp: dict):
+    """Time the CPU oracle on host copies of one bucket's inputs."""
+    import numpy as np
+    from oracle import zs_oracle as O
+
+    def host(x):
+        a = x.cpu().numpy()
+        return a.view(np.uint16) if a.dtype == np.int16 else a
+
+    hp_, m_, v_ = host(p), host(m), host(v)
+    cs = [host(c) for c in contribs]
+    n = hp_.size
+    t0 = time.perf_counter()
+    O.rank_step(hp_, m_, v_, cs, O.BF16, O.AdamWHP(step=t, **hp))
+    dt = time.perf_counter() - t0
+    return n / dt, dt, n
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="also run a plain 4 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+              "multi-GPU form of the shard step is a design, not a measured path.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fsdp_sharded_optimizer_zs_amd as zs
+    import workloads as W
+
+    zs.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.get("llama70b")
+    D = w.D
+    sizes = [zs.zs_unit_layout(u.numels, D)[3] for u in w.units]
+    S = int(sum(sizes))
+    starts = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    bmax = max(sizes)
+    hp = dict(W.ADAMW_HP)
+
+    log(f"allocating rank shard: S={S} ({S * 14 / 1e9:.1f} GB of p, m, v, w)")
+    p = torch.empty(S, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4000)
+    for a in range(0, S, 1 << 30):
+        b = min(S, a + (1 << 30))
+        torch.randn(b - a, generator=gen, device=dev, out=p[a:b]).mul_(W.PARAM_STD)
+    m = torch.zeros(S, device=dev)
+    v = torch.zeros(S, device=dev)
+    wshard = torch.empty(S, dtype=torch.int16, device=dev)
+    log(f"generating {CONTRIB_POOL} contribution sets of {D} x {bmax} bf16")
+    pool = torch.empty((CONTRIB_POOL, D, bmax), dtype=torch.int16, device=dev)
+    for s in range(CONTRIB_POOL):
+        for k in range(D):
+            pool[s, k].copy_(W.contribution(w, bmax, 1, s, k, dev))
+    peers = torch.empty((D - 1, bmax), dtype=torch.int16, device=dev)
+    peers.copy_(pool[0, 1:])                  # stand-in for the other ranks' shards
+    unit_buf = torch.empty(D * bmax, dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()
+
+    # wrap time: layout + pack of one block unit's fp32 master (timed apart)
+    blk = w.units[0]
+    ts = [t.reshape(-1) for t in W.tensor_values(blk, "f32", 1, dev)]
+    bshards = [torch.empty(sizes[0], device=dev) for _ in range(D)]
+    zs.zs_pack_flat(ts, D, bshards)            # warm
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    zs.zs_pack_flat(ts, D, bshards)
+    e1.record()
+    torch.cuda.synchronize()
+    pack_ms = e0.elapsed_time(e1)
+    pack_bytes = 2 * 4 * blk.numel
+    del ts, bshards
+    torch.cuda.empty_cache()
+
+    buckets = []
+    for b, sz in enumerate(sizes):
+        sl = slice(int(starts[b]), int(starts[b + 1]))
+        cs = [pool[b % CONTRIB_POOL, k, :sz] for k in range(D)]
+        shards = [wshard[sl]] + [peers[r, :sz] for r in range(D - 1)]
+        buckets.append((sl, sz, cs, shards, unit_buf[:D * sz]))
+
+    n_launch = len(buckets)
+    K = args.steps
+    # one event triple per (timed step, bucket), read only after the timed region
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_launch)]
+          for _ in range(K)]
+
+    def step(t: int, evs):
+        h = zs.AdamWHP(step=t, **hp)
+        for i, (sl, sz, cs, shards, ubuf) in enumerate(buckets):
+            if evs:
+                evs[i][0].record()
+            zs.zs_adamw_step(p[sl], m[sl], v[sl], wshard[sl], cs, h)
+            if evs:
+                evs[i][1].record()
+            zs.zs_gather_unit(shards, ubuf)
+            if evs:
+                evs[i][2].record()
+
+    log(f"warmup {args.warmup} step(s)")
+    for t in range(1, args.warmup + 1):
+        step(t, None)
+    torch.cuda.synchronize()
+    log(f"timing {K} step(s) of {n_launch} units")
+    t0 = time.perf_counter()
+    for j in range(K):
+        step(args.warmup + 1 + j, ev[j])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    adam_ms = sum(e[0].elapsed_time(e[1]) for evs in ev for e in evs)
+    gather_ms = sum(e[1].elapsed_time(e[2]) for evs in ev for e in evs)
+    ms_per_step = elapsed * 1e3 / K
+    log(f"{ms_per_step:.2f} ms/step")
+
+    es = 2
+    bpp = 26 + D * es                              # fused: 12 read + 14 written + D*es
+    adam_launches = K * n_launch
+    adam_avg_s = adam_ms / 1e3 / adam_launches
+    bytes_per_launch = bpp * S / n_launch
+    achieved = bytes_per_launch / adam_avg_s / 1e9
+    gather_bytes = 4.0 * D * S                     # D*S bf16 read + written per step
+    traffic = traffic_from_profiles(bytes_per_launch)
+    out = {
+        "metric": METRIC,
+        "value": S * K / elapsed,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama70b rank-0 shard, D=8, 81 unit buckets (80 blocks + root), "
+                        "fused reduce+AdamW then unit all-gather rebuild per bucket",
+            "shard_params": S, "D": D, "reduce_dtype": "bf16", "param_dtype": "bf16",
+            "master_dtype": "f32", "buckets": n_launch,
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "adamw_vec_kernel<bf16,8>",
+            "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_param": bpp,
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+            "avg_launch_ms": adam_avg_s * 1e3,
+        },
+        "adamw_fused": {"params_per_s": S * K / (adam_ms / 1e3),
+                        "ms_per_step": adam_ms / K, "GB_s": achieved},
+        "gather": {"ms_per_step": gather_ms / K,
+                   "GB_s": gather_bytes * K / (gather_ms / 1e3) / 1e9},
+        "wrap": {"pack_block_unit_f32_ms": pack_ms,
+                 "pack_GB_s": pack_bytes / (pack_ms / 1e3) / 1e9},
+    }
+    if args.copy_calibrate:
+        a = torch.empty(1 << 30, device=dev)          # 4 GiB fp32
+        bb = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        bb.copy_(a)
+        c1.record()
+        torch.cuda.synchronize()
+        out["copy_4GiB"] = {"ms": c0.elapsed_time(c1),
+                            "GB_s": 2 * 4 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9}
+        del a, bb
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on one block bucket (host copies)")
+        sl, sz, cs, _, _ = buckets[0]
+        # one step of the oracle from the bucket's current state
+        rate, secs, n = cpu_baseline(p[sl], m[sl], v[sl], cs, args.warmup + K + 1, hp)
+        out["cpu_baseline"] = {
+            "value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"one block bucket of the same workload ({n} params, D=8 bf16 "
+                      f"contributions), one step, {secs:.1f} s of single-threaded numpy",
+        }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,248 @@
+"""ctypes binding of libzs.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls (include/zs.h) and
+takes torch tensors for device buffers; it checks that they are contiguous
+device tensors of the right dtype and length, turns them into raw pointers
+and the current stream, and raises ZsError on a nonzero status. All work of
+the shard step runs in the library's HIP kernels. There is no fallback: if
+the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import threading
+from typing import List, Sequence, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzs.so")
+
+ZS_OK, ZS_EINVAL, ZS_EALIAS, ZS_EHIP, ZS_EUNSUPPORTED = 0, 1, 2, 3, 4
+ZS_BF16, ZS_F32 = 1, 2
+ZS_MAX_D = 64
+
+
+class ZsError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libzs status {status}: {message}")
+        self.status = status
+
+
+class zs_tensor_ref(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("numel", ctypes.c_int64),
+                ("flat_offset", ctypes.c_int64)]
+
+
+class zs_adamw_hp(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64)]
+
+
+@dataclasses.dataclass(frozen=True)
+class AdamWHP:
+    lr: float
+    beta1: float
+    beta2: float
+    eps: float
+    weight_decay: float
+    step: int
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libzs.so (once). Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with "
+                    "`python -m fsdp_sharded_optimizer_zs_amd.build` (needs hipcc)")
+            lib = ctypes.CDLL(LIB_PATH)
+            i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+            P = ctypes.POINTER
+            sig = {
+                "zs_unit_layout": (i32, [P(i64), i32, i32, P(i64), P(i64), P(i64), P(i64)]),
+                "zs_pack_flat": (i32, [P(zs_tensor_ref), vp, i32, i32, i32, P(vp), i64, vp]),
+                "zs_reduce_shard": (i32, [P(vp), i32, i32, i64, vp, vp]),
+                "zs_adamw_step": (i32, [vp, vp, vp, vp, i64, P(vp), i32, i32,
+                                        P(zs_adamw_hp), vp]),
+                "zs_gather_unit": (i32, [P(vp), i32, i64, i32, vp, vp]),
+                "zs_last_error": (ctypes.c_char_p, []),
+                "zs_abi_version": (i32, []),
+            }
+            for name, (res, args) in sig.items():
+                f = getattr(lib, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != ZS_OK:
+        raise ZsError(status, load().zs_last_error().decode())
+
+
+def zs_last_error() -> str:
+    return load().zs_last_error().decode()
+
+
+def zs_abi_version() -> int:
+    return int(load().zs_abi_version())
+
+
+# ------------------------------------------------------------------ helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype in (torch.bfloat16, torch.int16) or t.dtype == getattr(torch, "uint16", None):
+        return ZS_BF16
+    if t.dtype == torch.float32:
+        return ZS_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bf16 (bfloat16/int16 bits) or float32")
+
+
+def _dev(t, what: str):
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device (cuda/HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    return ctypes.c_void_p(_torch().cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr_array(ts: Sequence) -> ctypes.Array:
+    arr = (ctypes.c_void_p * max(1, len(ts)))()
+    for i, t in enumerate(ts):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def _hp(hp) -> zs_adamw_hp:
+    if isinstance(hp, dict):
+        hp = AdamWHP(**hp)
+    return zs_adamw_hp(float(hp.lr), float(hp.beta1), float(hp.beta2), float(hp.eps),
+                       float(hp.weight_decay), int(hp.step))
+
+
+# --------------------------------------------------------------- entry points
+def zs_unit_layout(numels: Sequence[int], D: int) -> Tuple[List[int], int, int, int]:
+    """(offsets[T+1], N, N_pad, S) of a unit; host arithmetic in the library."""
+    lib = load()
+    T = len(numels)
+    arr = (ctypes.c_int64 * max(1, T))(*[int(n) for n in numels])
+    off = (ctypes.c_int64 * (T + 1))()
+    n, npad, s = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.zs_unit_layout(arr, T, int(D), off, ctypes.byref(n), ctypes.byref(npad),
+                              ctypes.byref(s)))
+    return list(off), n.value, npad.value, s.value
+
+
+def zs_pack_flat(tensors: Sequence, D: int, shards: Sequence, stream=None):
+    """Pack tensors (all bf16 or all fp32, contiguous, on the device) into D
+    shard tensors of S elements each. Returns the device tensor table, which
+    the enqueued kernel reads (stream-ordered; keep it or let torch's
+    caching allocator recycle it on the same stream)."""
+    torch = _torch()
+    if len(shards) != D:
+        raise ValueError("need exactly D shard tensors")
+    ref = shards[0]
+    code = _dtype_code(ref)
+    for i, t in enumerate(list(tensors) + list(shards)):
+        _dev(t, f"tensor {i}")
+        if _dtype_code(t) != code or t.element_size() != ref.element_size():
+            raise TypeError("tensors and shards must share one element type")
+    offsets, N, _, S = zs_unit_layout([t.numel() for t in tensors], D)
+    if any(s.numel() != S for s in shards):
+        raise ValueError(f"every shard must hold S = {S} elements")
+    T = len(tensors)
+    h = (zs_tensor_ref * max(1, T))()
+    rows = []
+    for j, t in enumerate(tensors):
+        h[j] = zs_tensor_ref(t.data_ptr(), t.numel(), offsets[j])
+        rows.append((t.data_ptr(), t.numel(), offsets[j]))
+    d_table = (torch.tensor(rows, dtype=torch.int64) if rows
+               else torch.zeros((0, 3), dtype=torch.int64)).to(ref.device)
+    _check(load().zs_pack_flat(h, ctypes.c_void_p(d_table.data_ptr() if T else None), T, code,
+                               int(D), _ptr_array(shards), S, _stream(ref, stream)))
+    return d_table
+
+
+def zs_reduce_shard(contribs: Sequence, grad_out, stream=None) -> None:
+    """grad_out (fp32, S) = mean of the contributions, folded in rank order."""
+    S = grad_out.numel()
+    _dev(grad_out, "grad_out")
+    if grad_out.dtype != _torch().float32:
+        raise TypeError("grad_out must be float32")
+    code = _dtype_code(contribs[0]) if contribs else ZS_F32
+    for i, c in enumerate(contribs):
+        _dev(c, f"contribs[{i}]")
+        if c.numel() != S or _dtype_code(c) != code:
+            raise ValueError("contributions must share one dtype and hold S elements")
+    _check(load().zs_reduce_shard(_ptr_array(contribs), len(contribs), code, S,
+                                  ctypes.c_void_p(grad_out.data_ptr()),
+                                  _stream(grad_out, stream)))
+
+
+def zs_adamw_step(p, m, v, w_out, contribs: Sequence, hp, stream=None) -> None:
+    """Fused reduce + AdamW on one shard: p, m, v in place, w_out (bf16) written."""
+    torch = _torch()
+    S = p.numel()
+    for name, t in (("p", p), ("m", m), ("v", v)):
+        _dev(t, name)
+        if t.dtype != torch.float32 or t.numel() != S:
+            raise ValueError(f"{name} must be float32 with S = {S} elements")
+    _dev(w_out, "w_out")
+    if _dtype_code(w_out) != ZS_BF16 or w_out.numel() != S:
+        raise ValueError("w_out must be bf16 bits with S elements")
+    code = _dtype_code(contribs[0]) if contribs else ZS_F32
+    for i, c in enumerate(contribs):
+        _dev(c, f"contribs[{i}]")
+        if c.numel() != S or _dtype_code(c) != code:
+            raise ValueError("contributions must share one dtype and hold S elements")
+    h = _hp(hp)
+    _check(load().zs_adamw_step(ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(m.data_ptr()),
+                                ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(w_out.data_ptr()),
+                                S, _ptr_array(contribs), len(contribs), code,
+                                ctypes.byref(h), _stream(p, stream)))
+
+
+def zs_gather_unit(shards: Sequence, flat_out, stream=None) -> None:
+    """flat_out[r*S + i] = shards[r][i]."""
+    D = len(shards)
+    _dev(flat_out, "flat_out")
+    S = shards[0].numel() if shards else 0
+    code = _dtype_code(flat_out)
+    for i, s in enumerate(shards):
+        _dev(s, f"shards[{i}]")
+        if s.numel() != S or _dtype_code(s) != code:
+            raise ValueError("shards must share one dtype and length")
+    if flat_out.numel() != D * S:
+        raise ValueError(f"flat_out must hold D*S = {D * S} elements")
+    _check(load().zs_gather_unit(_ptr_array(shards), D, S, code,
+                                 ctypes.c_void_p(flat_out.data_ptr()), _stream(flat_out, stream)))
+
+
+# Raw-pointer forms, for callers that manage device memory themselves.
+def raw_adamw_step(p: int, m: int, v: int, w: int, S: int, contribs: Sequence[int],
+                   dtype: int, hp, stream: int) -> None:
+    arr = (ctypes.c_void_p * max(1, len(contribs)))(*contribs)
+    h = _hp(hp)
+    _check(load().zs_adamw_step(ctypes.c_void_p(p), ctypes.c_void_p(m), ctypes.c_void_p(v),
+                                ctypes.c_void_p(w), int(S), arr, len(contribs), int(dtype),
+                                ctypes.byref(h), ctypes.c_void_p(stream)))

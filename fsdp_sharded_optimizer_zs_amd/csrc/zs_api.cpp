@@ -1,0 +1,292 @@
+// C-ABI entry points of libzs: host-side validation, layout arithmetic and
+// the fp32 constants of the AdamW step, then one kernel launch on the
+// caller's stream. Nothing here allocates device memory or synchronizes.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "zs_internal.h"
+
+#define ZS_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace zs {
+namespace {
+
+thread_local std::string g_last_error;
+
+zs_status fail(zs_status code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+zs_status ok() {
+    g_last_error.clear();
+    return ZS_OK;
+}
+
+zs_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(ZS_EHIP, "%s: HIP error %d (%s)", what, int(e), hipGetErrorString(e));
+}
+
+int elem_size(int32_t dtype) {
+    if (dtype == ZS_BF16) return 2;
+    if (dtype == ZS_F32) return 4;
+    return 0;
+}
+
+// Byte range [lo, hi) of a buffer, for overlap checks.
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, int64_t count, int es) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + uintptr_t(count) * uintptr_t(es)};
+}
+
+bool overlap(const Range& a, const Range& b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Elements S with S * es bytes representable (and addressable) on the host.
+bool size_ok(int64_t S, int es) { return S >= 0 && S <= (INT64_MAX / 16) / es; }
+
+// Fill a PtrPack from a host array of n device pointers, checking each.
+zs_status take_ptrs(const void* const* src, int n, int es, const char* what, PtrPack* out) {
+    if (src == nullptr) return fail(ZS_EINVAL, "%s: pointer array is NULL", what);
+    for (int i = 0; i < ZS_MAX_D; ++i) out->p[i] = nullptr;
+    for (int i = 0; i < n; ++i) {
+        if (src[i] == nullptr) return fail(ZS_EINVAL, "%s[%d] is NULL", what, i);
+        if (!aligned(src[i], uintptr_t(es)))
+            return fail(ZS_EINVAL, "%s[%d] is not aligned to its %d-byte elements", what, i, es);
+        out->p[i] = src[i];
+    }
+    return ZS_OK;
+}
+
+}  // namespace
+
+const DeviceInfo& device_info() {
+    static std::mutex mu;
+    static std::vector<DeviceInfo> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache.size() <= size_t(dev)) cache.resize(size_t(dev) + 1, DeviceInfo{0});
+    DeviceInfo& d = cache[size_t(dev)];
+    if (d.cu_count == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cu <= 0)
+            cu = 256;
+        d.cu_count = cu;
+    }
+    return d;
+}
+
+}  // namespace zs
+
+using namespace zs;
+
+ZS_EXPORT const char* zs_last_error(void) { return g_last_error.c_str(); }
+
+ZS_EXPORT int32_t zs_abi_version(void) { return 100; }
+
+ZS_EXPORT zs_status zs_unit_layout(const int64_t* numels, int32_t T, int32_t D,
+                                   int64_t* offsets_out, int64_t* n_out, int64_t* n_pad_out,
+                                   int64_t* shard_len_out) {
+    if (T < 0) return fail(ZS_EINVAL, "zs_unit_layout: T = %d < 0", T);
+    if (D < 1 || D > ZS_MAX_D)
+        return fail(ZS_EINVAL, "zs_unit_layout: D = %d outside 1..%d", D, ZS_MAX_D);
+    if (T > 0 && numels == nullptr) return fail(ZS_EINVAL, "zs_unit_layout: numels is NULL");
+    if (!offsets_out || !n_out || !n_pad_out || !shard_len_out)
+        return fail(ZS_EINVAL, "zs_unit_layout: an output pointer is NULL");
+    int64_t off = 0;
+    offsets_out[0] = 0;
+    for (int32_t j = 0; j < T; ++j) {
+        if (numels[j] < 0)
+            return fail(ZS_EINVAL, "zs_unit_layout: numels[%d] = %lld < 0", j, (long long)numels[j]);
+        if (numels[j] > INT64_MAX / 16 - off)
+            return fail(ZS_EUNSUPPORTED, "zs_unit_layout: unit size overflows");
+        off += numels[j];
+        offsets_out[j + 1] = off;
+    }
+    const int64_t S = off / D + (off % D != 0 ? 1 : 0);
+    *n_out = off;
+    *shard_len_out = S;
+    *n_pad_out = S * D;
+    return ok();
+}
+
+ZS_EXPORT zs_status zs_pack_flat(const zs_tensor_ref* h_table, const zs_tensor_ref* d_table,
+                                 int32_t T, int32_t dtype, int32_t D, void* const* shards,
+                                 int64_t S, hipStream_t stream) {
+    const int es = elem_size(dtype);
+    if (es == 0) return fail(ZS_EUNSUPPORTED, "zs_pack_flat: unknown dtype %d", dtype);
+    if (T < 0) return fail(ZS_EINVAL, "zs_pack_flat: T = %d < 0", T);
+    if (D < 1 || D > ZS_MAX_D)
+        return fail(ZS_EINVAL, "zs_pack_flat: D = %d outside 1..%d", D, ZS_MAX_D);
+    if (!size_ok(S, es) || S > INT64_MAX / 16 / D)
+        return fail(ZS_EINVAL, "zs_pack_flat: S = %lld out of range", (long long)S);
+    if (T > 0 && (h_table == nullptr || d_table == nullptr))
+        return fail(ZS_EINVAL, "zs_pack_flat: tensor table is NULL");
+    int64_t N = 0;
+    for (int32_t j = 0; j < T; ++j) {
+        const zs_tensor_ref& t = h_table[j];
+        if (t.numel < 0)
+            return fail(ZS_EINVAL, "zs_pack_flat: tensor %d has numel %lld", j, (long long)t.numel);
+        if (t.flat_offset != N)
+            return fail(ZS_EINVAL, "zs_pack_flat: tensor %d flat_offset %lld, expected %lld", j,
+                        (long long)t.flat_offset, (long long)N);
+        if (t.numel > 0 && t.ptr == nullptr)
+            return fail(ZS_EINVAL, "zs_pack_flat: tensor %d pointer is NULL", j);
+        if (!aligned(t.ptr, uintptr_t(es)))
+            return fail(ZS_EINVAL, "zs_pack_flat: tensor %d not aligned to %d bytes", j, es);
+        if (t.numel > INT64_MAX / 16 - N) return fail(ZS_EUNSUPPORTED, "zs_pack_flat: N overflows");
+        N += t.numel;
+    }
+    const int64_t want_S = N / D + (N % D != 0 ? 1 : 0);
+    if (S != want_S)
+        return fail(ZS_EINVAL, "zs_pack_flat: S = %lld but ceil(N/D) = %lld (N = %lld, D = %d)",
+                    (long long)S, (long long)want_S, (long long)N, D);
+    if (S == 0) return ok();
+    PtrPack sp;
+    zs_status st = take_ptrs(shards, D, es, "zs_pack_flat: shards", &sp);
+    if (st != ZS_OK) return st;
+    for (int r = 0; r < D; ++r) {
+        const Range a = range_of(sp.p[r], S, es);
+        for (int q = r + 1; q < D; ++q)
+            if (overlap(a, range_of(sp.p[q], S, es)))
+                return fail(ZS_EALIAS, "zs_pack_flat: shards %d and %d overlap", r, q);
+        for (int32_t j = 0; j < T; ++j)
+            if (overlap(a, range_of(h_table[j].ptr, h_table[j].numel, es)))
+                return fail(ZS_EALIAS, "zs_pack_flat: shard %d overlaps tensor %d", r, j);
+        if (overlap(a, range_of(d_table, T, int(sizeof(zs_tensor_ref)))))
+            return fail(ZS_EALIAS, "zs_pack_flat: shard %d overlaps the device table", r);
+    }
+    return hip_status(launch_pack(d_table, T, N, es, D, sp, S, stream), "zs_pack_flat launch");
+}
+
+ZS_EXPORT zs_status zs_reduce_shard(const void* const* contribs, int32_t D, int32_t dtype,
+                                    int64_t S, float* grad_out, hipStream_t stream) {
+    const int es = elem_size(dtype);
+    if (es == 0) return fail(ZS_EUNSUPPORTED, "zs_reduce_shard: unknown dtype %d", dtype);
+    if (D < 1 || D > ZS_MAX_D)
+        return fail(ZS_EINVAL, "zs_reduce_shard: D = %d outside 1..%d", D, ZS_MAX_D);
+    if (!size_ok(S, 4)) return fail(ZS_EINVAL, "zs_reduce_shard: S = %lld out of range", (long long)S);
+    if (S == 0) return ok();
+    if (grad_out == nullptr) return fail(ZS_EINVAL, "zs_reduce_shard: grad_out is NULL");
+    if (!aligned(grad_out, 4)) return fail(ZS_EINVAL, "zs_reduce_shard: grad_out not 4-byte aligned");
+    PtrPack cp;
+    zs_status st = take_ptrs(contribs, D, es, "zs_reduce_shard: contribs", &cp);
+    if (st != ZS_OK) return st;
+    const Range out = range_of(grad_out, S, 4);
+    bool al = aligned(grad_out, 16);
+    for (int k = 0; k < D; ++k) {
+        if (overlap(out, range_of(cp.p[k], S, es)))
+            return fail(ZS_EALIAS, "zs_reduce_shard: grad_out overlaps contribution %d", k);
+        al = al && aligned(cp.p[k], 16);
+    }
+    const float inv_n = float(1.0 / double(D));
+    return hip_status(launch_reduce(cp, D, dtype, S, inv_n, grad_out, al, stream),
+                      "zs_reduce_shard launch");
+}
+
+ZS_EXPORT zs_status zs_adamw_step(float* p, float* m, float* v, uint16_t* w_out, int64_t S,
+                                  const void* const* contribs, int32_t n_contrib, int32_t dtype,
+                                  const zs_adamw_hp* hp, hipStream_t stream) {
+    const int es = elem_size(dtype);
+    if (es == 0) return fail(ZS_EUNSUPPORTED, "zs_adamw_step: unknown dtype %d", dtype);
+    if (n_contrib < 1 || n_contrib > ZS_MAX_D)
+        return fail(ZS_EINVAL, "zs_adamw_step: n_contrib = %d outside 1..%d", n_contrib, ZS_MAX_D);
+    if (!size_ok(S, 4)) return fail(ZS_EINVAL, "zs_adamw_step: S = %lld out of range", (long long)S);
+    if (hp == nullptr) return fail(ZS_EINVAL, "zs_adamw_step: hp is NULL");
+    if (hp->step < 1) return fail(ZS_EINVAL, "zs_adamw_step: step = %lld < 1", (long long)hp->step);
+    if (!(std::isfinite(hp->lr) && hp->lr >= 0.0))
+        return fail(ZS_EINVAL, "zs_adamw_step: lr must be finite and >= 0");
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+        return fail(ZS_EINVAL, "zs_adamw_step: betas must lie in [0, 1)");
+    if (!(std::isfinite(hp->eps) && hp->eps >= 0.0))
+        return fail(ZS_EINVAL, "zs_adamw_step: eps must be finite and >= 0");
+    if (!(std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.0))
+        return fail(ZS_EINVAL, "zs_adamw_step: weight_decay must be finite and >= 0");
+    if (S == 0) return ok();
+    if (!p || !m || !v || !w_out) return fail(ZS_EINVAL, "zs_adamw_step: p, m, v or w_out is NULL");
+    if (!aligned(p, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(w_out, 2))
+        return fail(ZS_EINVAL, "zs_adamw_step: p, m, v or w_out misaligned for its element type");
+    PtrPack cp;
+    zs_status st = take_ptrs(contribs, n_contrib, es, "zs_adamw_step: contribs", &cp);
+    if (st != ZS_OK) return st;
+    const Range rs[4] = {range_of(p, S, 4), range_of(m, S, 4), range_of(v, S, 4),
+                         range_of(w_out, S, 2)};
+    const char* names[4] = {"p", "m", "v", "w_out"};
+    for (int a = 0; a < 4; ++a)
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(rs[a], rs[b]))
+                return fail(ZS_EALIAS, "zs_adamw_step: %s overlaps %s", names[a], names[b]);
+    bool al = aligned(p, 16) && aligned(m, 16) && aligned(v, 16) && aligned(w_out, 16);
+    for (int k = 0; k < n_contrib; ++k) {
+        const Range c = range_of(cp.p[k], S, es);
+        for (int a = 0; a < 4; ++a)
+            if (overlap(c, rs[a]))
+                return fail(ZS_EALIAS, "zs_adamw_step: contribution %d overlaps %s", k, names[a]);
+        al = al && aligned(cp.p[k], 16);
+    }
+
+    // Constants: double arithmetic, each rounded to fp32 once.
+    double b1t = 1.0, b2t = 1.0;
+    for (int64_t t = 0; t < hp->step; ++t) {
+        b1t = b1t * hp->beta1;
+        b2t = b2t * hp->beta2;
+        // Below 2^-54, 1 - b rounds to exactly 1.0 in double, so more
+        // factors cannot change any constant derived from b1t or b2t.
+        if (b1t < 0x1p-54 && b2t < 0x1p-54) break;
+    }
+    AdamConsts k;
+    k.dec = float(1.0 - hp->lr * hp->weight_decay);
+    k.b1 = float(hp->beta1);
+    k.b1c = float(1.0 - hp->beta1);
+    k.b2 = float(hp->beta2);
+    k.b2c = float(1.0 - hp->beta2);
+    k.ss = float(hp->lr / (1.0 - b1t));
+    k.bc2s = float(std::sqrt(1.0 - b2t));
+    k.eps = float(hp->eps);
+    k.inv_n = float(1.0 / double(n_contrib));
+    return hip_status(launch_adamw(p, m, v, w_out, S, cp, n_contrib, dtype, k, al, stream),
+                      "zs_adamw_step launch");
+}
+
+ZS_EXPORT zs_status zs_gather_unit(const void* const* shards, int32_t D, int64_t S,
+                                   int32_t dtype, void* flat_out, hipStream_t stream) {
+    const int es = elem_size(dtype);
+    if (es == 0) return fail(ZS_EUNSUPPORTED, "zs_gather_unit: unknown dtype %d", dtype);
+    if (D < 1 || D > ZS_MAX_D)
+        return fail(ZS_EINVAL, "zs_gather_unit: D = %d outside 1..%d", D, ZS_MAX_D);
+    if (!size_ok(S, es) || S > INT64_MAX / 16 / D)
+        return fail(ZS_EINVAL, "zs_gather_unit: S = %lld out of range", (long long)S);
+    if (S == 0) return ok();
+    if (flat_out == nullptr) return fail(ZS_EINVAL, "zs_gather_unit: flat_out is NULL");
+    if (!aligned(flat_out, uintptr_t(es)))
+        return fail(ZS_EINVAL, "zs_gather_unit: flat_out not aligned to %d bytes", es);
+    PtrPack sp;
+    zs_status st = take_ptrs(shards, D, es, "zs_gather_unit: shards", &sp);
+    if (st != ZS_OK) return st;
+    const Range out = range_of(flat_out, S * D, es);
+    for (int r = 0; r < D; ++r)
+        if (overlap(out, range_of(sp.p[r], S, es)))
+            return fail(ZS_EALIAS, "zs_gather_unit: flat_out overlaps shard %d", r);
+    return hip_status(launch_gather(sp, D, S, es, flat_out, stream), "zs_gather_unit launch");
+}

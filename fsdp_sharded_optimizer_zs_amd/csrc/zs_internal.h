@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI layer (zs_api.cpp) and the kernel
+// translation units. Not installed; the public interface is include/zs.h.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "../../include/zs.h"
+
+namespace zs {
+
+// Up to ZS_MAX_D device pointers passed by value as a kernel argument.
+struct PtrPack {
+    const void* p[ZS_MAX_D];
+};
+
+// fp32 constants of one AdamW step (rounded once from double on the host).
+struct AdamConsts {
+    float dec;    // 1 - lr * weight_decay
+    float b1;     // beta1
+    float b1c;    // 1 - beta1
+    float b2;     // beta2
+    float b2c;    // 1 - beta2
+    float ss;     // lr / (1 - beta1^t)
+    float bc2s;   // sqrt(1 - beta2^t)
+    float eps;    // eps
+    float inv_n;  // 1 / n_contrib
+};
+
+// Launch geometry of the device the caller's stream runs on.
+struct DeviceInfo {
+    int cu_count;
+};
+const DeviceInfo& device_info();
+
+// Kernel launchers (enqueue only; return the launch status).
+hipError_t launch_adamw(float* p, float* m, float* v, uint16_t* w, int64_t S,
+                        const PtrPack& contribs, int n, int dtype,
+                        const AdamConsts& k, bool aligned, hipStream_t stream);
+hipError_t launch_reduce(const PtrPack& contribs, int n, int dtype, int64_t S,
+                         float inv_n, float* out, bool aligned, hipStream_t stream);
+hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es,
+                       int D, const PtrPack& shards, int64_t S, hipStream_t stream);
+hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es,
+                         void* flat, hipStream_t stream);
+
+}  // namespace zs

@@ -1,0 +1,164 @@
+// Pack (flat unit -> D shards) and gather (D shards -> flat unit) for gfx950.
+//
+// Both are bit copies bound by HBM bandwidth. Work is split into runs that
+// are contiguous on both sides (a tensor piece that lands inside one shard,
+// or one shard landing in the flat unit). Lanes write whole 16-byte
+// destination vectors (dwordx4 stores); the source is read with dwordx4
+// loads when it is 16-byte aligned relative to the destination and with
+// narrower, still coalesced, loads otherwise. The few elements before the
+// first and after the last aligned vector of a run are copied one per lane.
+// No lane ever touches a byte outside the run it copies.
+
+#include "zs_internal.h"
+
+#ifndef ZS_BLOCKS_PER_CU
+#define ZS_BLOCKS_PER_CU 8
+#endif
+
+namespace zs {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int64_t kPackChunk = 16384;  // flat elements per pack work item
+
+template <int ES>
+struct Elem;
+template <>
+struct Elem<2> {
+    using T = uint16_t;
+};
+template <>
+struct Elem<4> {
+    using T = uint32_t;
+};
+
+// Copy n elements of ES bytes from src to dst. The calling threads are
+// numbered tid in [0, nthr); each element is written by exactly one of them.
+template <int ES>
+__device__ __forceinline__ void copy_run(char* dst, const char* src, int64_t n, int64_t tid,
+                                         int64_t nthr) {
+    using T = typename Elem<ES>::T;
+    constexpr int V = 16 / ES;
+    int64_t head = int64_t((16 - (reinterpret_cast<uintptr_t>(dst) & 15)) & 15) / ES;
+    if (head > n) head = n;
+    const int64_t body = (n - head) / V;
+    const int64_t tail = n - head - body * V;
+    if (tid < head) {
+        reinterpret_cast<T*>(dst)[tid] = reinterpret_cast<const T*>(src)[tid];
+    } else if (tid - head < tail) {
+        const int64_t e = head + body * V + (tid - head);
+        reinterpret_cast<T*>(dst)[e] = reinterpret_cast<const T*>(src)[e];
+    }
+    u32x4* db = reinterpret_cast<u32x4*>(dst + head * ES);
+    const char* sb = src + head * ES;
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(sb);
+    if ((sa & 15) == 0) {
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(sb);
+        for (int64_t i = tid; i < body; i += nthr) db[i] = __builtin_nontemporal_load(s4 + i);
+    } else if ((sa & 3) == 0) {
+        const uint32_t* s1 = reinterpret_cast<const uint32_t*>(sb);
+        for (int64_t i = tid; i < body; i += nthr) {
+            const uint32_t* s = s1 + 4 * i;
+            db[i] = u32x4{s[0], s[1], s[2], s[3]};
+        }
+    } else {  // 2-byte elements at an odd element offset
+        const uint16_t* s1 = reinterpret_cast<const uint16_t*>(sb);
+        for (int64_t i = tid; i < body; i += nthr) {
+            const uint16_t* s = s1 + 8 * i;
+            u32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = uint32_t(s[2 * e]) | (uint32_t(s[2 * e + 1]) << 16);
+            db[i] = x;
+        }
+    }
+}
+
+// Pack: work item q covers flat[lo, hi) inside shard r = q / per_shard. The
+// block finds the first tensor ending after lo (binary search on the table),
+// copies each tensor piece overlapping [lo, hi), then zero-fills [N, hi).
+template <int ES>
+__global__ __launch_bounds__(kThreads) void pack_kernel(const zs_tensor_ref* __restrict__ table,
+                                                        int T, int64_t N, PtrPack shards,
+                                                        int64_t S, int64_t per_shard,
+                                                        int64_t items) {
+    using Tv = typename Elem<ES>::T;
+    for (int64_t q = blockIdx.x; q < items; q += gridDim.x) {
+        const int64_t r = q / per_shard;
+        const int64_t base = r * S;
+        const int64_t lo = base + (q - r * per_shard) * kPackChunk;
+        const int64_t hi = lo + kPackChunk < base + S ? lo + kPackChunk : base + S;
+        char* shard = static_cast<char*>(const_cast<void*>(shards.p[r]));
+        // smallest j with flat_offset_j + numel_j > lo
+        int a = 0, b = T;
+        while (a < b) {
+            const int mid = (a + b) >> 1;
+            if (table[mid].flat_offset + table[mid].numel > lo) b = mid;
+            else a = mid + 1;
+        }
+        for (int j = a; j < T; ++j) {
+            const int64_t off = table[j].flat_offset;
+            if (off >= hi) break;
+            const int64_t s0 = off > lo ? off : lo;
+            const int64_t end = off + table[j].numel;
+            const int64_t s1 = end < hi ? end : hi;
+            if (s1 > s0) {
+                copy_run<ES>(shard + (s0 - base) * ES,
+                             static_cast<const char*>(table[j].ptr) + (s0 - off) * ES, s1 - s0,
+                             threadIdx.x, kThreads);
+            }
+        }
+        if (hi > N) {
+            const int64_t z0 = N > lo ? N : lo;
+            for (int64_t e = z0 + threadIdx.x; e < hi; e += kThreads)
+                reinterpret_cast<Tv*>(shard)[e - base] = Tv(0);
+        }
+    }
+}
+
+// Gather: blockIdx.y = shard r, copied to flat[r*S, (r+1)*S).
+template <int ES>
+__global__ __launch_bounds__(kThreads) void gather_kernel(PtrPack shards, int64_t S,
+                                                          char* __restrict__ flat) {
+    const int r = blockIdx.y;
+    copy_run<ES>(flat + int64_t(r) * S * ES, static_cast<const char*>(shards.p[r]), S,
+                 int64_t(blockIdx.x) * kThreads + threadIdx.x, int64_t(gridDim.x) * kThreads);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es, int D,
+                       const PtrPack& shards, int64_t S, hipStream_t stream) {
+    const int64_t per_shard = (S + kPackChunk - 1) / kPackChunk;
+    const int64_t items = per_shard * D;
+    int64_t blocks = int64_t(device_info().cu_count) * ZS_BLOCKS_PER_CU;
+    if (blocks > items) blocks = items;
+    if (blocks < 1) blocks = 1;
+    if (es == 2)
+        hipLaunchKernelGGL((pack_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                           d_table, T, N, shards, S, per_shard, items);
+    else
+        hipLaunchKernelGGL((pack_kernel<4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                           d_table, T, N, shards, S, per_shard, items);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es, void* flat,
+                         hipStream_t stream) {
+    const int64_t vecs = (S * es + 15) / 16 + 1;
+    int64_t bx = (vecs + kThreads - 1) / kThreads;
+    const int64_t cap = (int64_t(device_info().cu_count) * ZS_BLOCKS_PER_CU + D - 1) / D;
+    if (bx > cap) bx = cap;
+    if (bx < 1) bx = 1;
+    char* f = static_cast<char*>(flat);
+    if (es == 2)
+        hipLaunchKernelGGL((gather_kernel<2>), dim3(unsigned(bx), unsigned(D)), dim3(kThreads), 0,
+                           stream, shards, S, f);
+    else
+        hipLaunchKernelGGL((gather_kernel<4>), dim3(unsigned(bx), unsigned(D)), dim3(kThreads), 0,
+                           stream, shards, S, f);
+    return hipGetLastError();
+}
+
+}  // namespace zs

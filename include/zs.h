@@ -1,0 +1,218 @@
+/*
+ * zs.h -- C ABI of the ZeRO-3 shard-step library (libzs.so) for MI355X (gfx950).
+ *
+ * One data-parallel rank's ZeRO-3 / FSDP shard step, with the D ranks of a
+ * data-parallel group simulated as D buffers in one GPU's memory:
+ *
+ *   zs_unit_layout   flat layout of one FSDP unit (host arithmetic only)
+ *   zs_pack_flat     pack a unit's tensors into D contiguous shards
+ *   zs_reduce_shard  reduce-scatter arithmetic for one shard
+ *   zs_adamw_step    fused reduce + mixed-precision AdamW on one shard
+ *   zs_gather_unit   all-gather's local rebuild of a unit from its shards
+ *
+ * Sources (web pages, by title and section):
+ *   [ZT]   "7.10 -- Fully-sharded data parallel (FSDP / ZeRO-3)", AI / ML
+ *          Theory, chapter 7.
+ *   [GPT8] "Building GPT from Scratch -- Part 8: FSDP -- When the Model
+ *          Won't Fit".
+ *   [RP]   "Distributed LLM Fine-Tuning at Scale: FSDP, ZeRO-3, and
+ *          Multi-GPU Orchestration".
+ *
+ * Conventions shared by every entry point:
+ *   - All data buffers are device memory owned by the caller. The library
+ *     never allocates, frees or synchronizes; kernels are enqueued on the
+ *     caller's stream (which must belong to the current HIP device) and the
+ *     call returns as soon as they are enqueued.
+ *   - Arrays of D pointers (shards, contributions) are HOST arrays of DEVICE
+ *     pointers; they are copied into kernel arguments, so D <= ZS_MAX_D.
+ *   - bf16 values are raw IEEE binary32 high halves stored as uint16.
+ *   - Every argument is validated on the host before anything is enqueued.
+ *     A failing call returns a nonzero status, enqueues nothing, and leaves
+ *     a message for zs_last_error(). A launch failure reported by the HIP
+ *     runtime returns ZS_EHIP. Faults of enqueued kernels surface at the
+ *     caller's next synchronization, as for any HIP kernel.
+ *   - Zero-length work (S == 0, T == 0) returns ZS_OK and enqueues nothing.
+ *   - Calls are thread-safe; the error message is per calling thread.
+ *   - Full-speed paths need 16-byte-aligned buffers; any other alignment
+ *     allowed by the element size is correct but slower.
+ */
+#ifndef ZS_H_
+#define ZS_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t zs_status;
+#define ZS_OK            0  /* success                                       */
+#define ZS_EINVAL        1  /* an argument is out of range or inconsistent   */
+#define ZS_EALIAS        2  /* an output overlaps an input it may not        */
+#define ZS_EHIP          3  /* the HIP runtime reported an error             */
+#define ZS_EUNSUPPORTED  4  /* unknown dtype or a size beyond the limits     */
+
+/* Element types. */
+#define ZS_BF16 1  /* bf16 as uint16 bit patterns (2 bytes)                   */
+#define ZS_F32  2  /* IEEE binary32 (4 bytes)                                 */
+
+#define ZS_MAX_D 64  /* most ranks (or contributions) one call handles       */
+
+/* One tensor of an FSDP unit: its data and where it lands in the flat unit. */
+typedef struct {
+    const void* ptr;      /* device pointer to numel contiguous elements      */
+    int64_t numel;        /* >= 0                                             */
+    int64_t flat_offset;  /* start in the flat unit: prefix sum of numels     */
+} zs_tensor_ref;
+
+/* AdamW hyperparameters, in double; the library rounds each derived
+ * constant to fp32 once (see zs_adamw_step). */
+typedef struct {
+    double lr;            /* >= 0                                             */
+    double beta1;         /* in [0, 1)                                        */
+    double beta2;         /* in [0, 1)                                        */
+    double eps;           /* >= 0                                             */
+    double weight_decay;  /* >= 0, decoupled, multiplied by lr               */
+    int64_t step;         /* t >= 1, the step being taken                     */
+} zs_adamw_hp;
+
+/*
+ * zs_unit_layout -- flat layout of one FSDP unit (host only, no GPU work).
+ *
+ * [ZT] section 3 gives each rank r a partition P_r of about 1/D of the
+ * parameters; [ZT] section 6 and [GPT8] "PyTorch FSDP Implementation" make
+ * each transformer block one unit. Layout: the T tensors end to end in the
+ * given order, no per-tensor alignment, the flat length N padded up to
+ * N_pad = D * ceil(N / D); rank r owns flat[r*S, (r+1)*S) with S = N_pad / D.
+ *
+ *   numels      host, T entries, each >= 0 (may be NULL when T == 0)
+ *   T           number of tensors, >= 0
+ *   D           ranks, 1..ZS_MAX_D
+ *   offsets_out host, T + 1 entries: offsets_out[j] = start of tensor j,
+ *               offsets_out[T] = N
+ *   n_out, n_pad_out, shard_len_out  host scalars: N, N_pad, S
+ * Errors: ZS_EINVAL for a negative count, a NULL output or D out of range;
+ * ZS_EUNSUPPORTED if N_pad overflows int64.
+ */
+zs_status zs_unit_layout(const int64_t* numels, int32_t T, int32_t D,
+                         int64_t* offsets_out, int64_t* n_out,
+                         int64_t* n_pad_out, int64_t* shard_len_out);
+
+/*
+ * zs_pack_flat -- pack a unit's tensors into its D shards (bit copy).
+ *
+ * The flat unit (layout of zs_unit_layout) is split into D contiguous
+ * shards, the rank-ordered blocks of the all-gather diagram in [GPT8]
+ * "AllGather vs AllReduce" and the local shards of [ZT] section 5.1:
+ * shards[r][i] = flat[r*S + i], with flat[N, N_pad) = +0 (all-zero bits).
+ * Bytes are copied unchanged whatever they hold.
+ *
+ *   h_table  host array of T tensor refs, checked by the library: numel >= 0,
+ *            ptr non-NULL when numel > 0 and aligned to the element size,
+ *            flat_offset equal to the prefix sum of the numels
+ *   d_table  device array holding the same T refs byte for byte (the kernel
+ *            reads this copy; the caller keeps it alive until the work is done)
+ *   T        tensors, >= 0
+ *   dtype    ZS_BF16 or ZS_F32 (element size of every tensor and shard)
+ *   D        ranks, 1..ZS_MAX_D
+ *   shards   host array of D device pointers, each to S elements
+ *   S        shard length; must equal ceil(N / D) for N = sum of numels
+ * Errors: ZS_EINVAL (inconsistent table, S, NULLs, alignment), ZS_EALIAS
+ * (a shard overlaps a tensor or another shard), ZS_EUNSUPPORTED (dtype).
+ */
+zs_status zs_pack_flat(const zs_tensor_ref* h_table, const zs_tensor_ref* d_table,
+                       int32_t T, int32_t dtype, int32_t D,
+                       void* const* shards, int64_t S, hipStream_t stream);
+
+/*
+ * zs_reduce_shard -- reduce-scatter arithmetic for one rank's shard.
+ *
+ * [GPT8] "AllGather vs AllReduce": rank r receives the sum over ranks of
+ * their gradients restricted to its shard; [ZT] section 4: this is the
+ * all-reduce's result, scattered; DDP's all-reduce averages. For i < S:
+ *   grad_out[i] = (((c_0[i] + c_1[i]) + ...) + c_{D-1}[i]) * float(1/D)
+ * in fp32, contributions widened exactly from the reduce dtype (bf16 as in
+ * [RP] section 2, or fp32 as in [GPT8] "Mixed Precision"), folded left to
+ * right in rank order starting from c_0, one rounding per add, then one
+ * multiply by 1/D rounded to fp32. The result stays fp32.
+ *
+ *   contribs  host array of D device pointers, each to S elements of dtype
+ *   D         contributions, 1..ZS_MAX_D
+ *   dtype     ZS_BF16 or ZS_F32
+ *   S         >= 0
+ *   grad_out  device, S floats
+ * Errors: ZS_EINVAL, ZS_EALIAS (grad_out overlaps a contribution),
+ * ZS_EUNSUPPORTED.
+ */
+zs_status zs_reduce_shard(const void* const* contribs, int32_t D, int32_t dtype,
+                          int64_t S, float* grad_out, hipStream_t stream);
+
+/*
+ * zs_adamw_step -- fused reduce + mixed-precision AdamW on one shard.
+ *
+ * [ZT] section 3: a rank updates only its partition, from its fp32 master
+ * copy, its m and v and its slice of the gradient; [ZT] section 6 and
+ * [GPT8] "Mixed Precision": master and moments stay fp32, the working
+ * weights are bf16. Per element, g is the zs_reduce_shard value of the
+ * n_contrib contributions (their mean, folded in order), never stored; then
+ * in fp32, each operation rounded on its own, no fused multiply-add:
+ *   p1  = p * DEC
+ *   m'  = B1 * m + B1c * g
+ *   v'  = B2 * v + B2c * (g * g)
+ *   den = sqrt(v') / BC2S + EPS
+ *   p'  = p1 - SS * (m' / den)
+ *   w   = bf16 round-to-nearest-even of p'
+ * with constants rounded to fp32 once from double: B1 = beta1,
+ * B1c = 1 - beta1, B2 = beta2, B2c = 1 - beta2, SS = lr / (1 - beta1^t),
+ * BC2S = sqrt(1 - beta2^t), DEC = 1 - lr * weight_decay, EPS = eps, where
+ * beta^t is t successive double multiplications starting from 1.0.
+ * An unfused step (zs_reduce_shard, then this call with its output as the
+ * single fp32 contribution) gives the same bits.
+ *
+ *   p, m, v   device, S floats each, updated in place (pairwise disjoint)
+ *   w_out     device, S uint16 (bf16 working shard), written
+ *   S         >= 0
+ *   contribs  host array of n_contrib device pointers, S elements of dtype
+ *   n_contrib 1..ZS_MAX_D
+ *   dtype     ZS_BF16 or ZS_F32
+ *   hp        host pointer to the hyperparameters
+ * Errors: ZS_EINVAL (NULLs, alignment, hyperparameters out of range),
+ * ZS_EALIAS (p, m, v, w_out overlap each other or a contribution),
+ * ZS_EUNSUPPORTED.
+ */
+zs_status zs_adamw_step(float* p, float* m, float* v, uint16_t* w_out, int64_t S,
+                        const void* const* contribs, int32_t n_contrib, int32_t dtype,
+                        const zs_adamw_hp* hp, hipStream_t stream);
+
+/*
+ * zs_gather_unit -- the local data movement of all-gather.
+ *
+ * [GPT8] "AllGather vs AllReduce": afterwards every rank holds all blocks in
+ * rank order; [ZT] section 5.1 gathers a block's shards into its full
+ * parameters before each forward and backward. For r < D, i < S:
+ *   flat_out[r*S + i] = shards[r][i]   (bit copy, padding included)
+ * Tensor j of the unit is then the view flat_out[off_j, off_j + numel_j).
+ *
+ *   shards    host array of D device pointers, each to S elements
+ *   D         1..ZS_MAX_D
+ *   S         >= 0
+ *   dtype     ZS_BF16 or ZS_F32
+ *   flat_out  device, D * S elements
+ * Errors: ZS_EINVAL, ZS_EALIAS (flat_out overlaps a shard), ZS_EUNSUPPORTED.
+ */
+zs_status zs_gather_unit(const void* const* shards, int32_t D, int64_t S,
+                         int32_t dtype, void* flat_out, hipStream_t stream);
+
+/* Text of the calling thread's most recent failure ("" if none). The pointer
+ * stays valid until the thread's next call into the library. */
+const char* zs_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t zs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZS_H_ */

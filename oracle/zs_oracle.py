@@ -126,6 +126,19 @@ def pack_flat(tensors: Sequence[np.ndarray], D: int) -> List[np.ndarray]:
     return [flat[r * S:(r + 1) * S].copy() for r in range(D)]
 
 
+def flat_source(offsets: Sequence[int], flat_index: np.ndarray):
+    """Where flat positions come from, by the definition of pack_flat: for
+    each flat index i returns (j, e) with i = offsets[j] + e, or j = -1 for
+    a pad position (i >= N). Empty tensors never own a position."""
+    offs = np.asarray(offsets, dtype=np.int64)
+    i = np.asarray(flat_index, dtype=np.int64)
+    j = np.searchsorted(offs, i, side="right") - 1
+    pad = i >= offs[-1]
+    j = np.where(pad, -1, j)
+    e = np.where(pad, 0, i - offs[np.maximum(j, 0)])
+    return j, e
+
+
 # --------------------------------------------------------------- O3: reduce
 def reduce_shard(contribs: Sequence[np.ndarray], dtype: str) -> np.ndarray:
     """Reduce-scatter arithmetic for one shard: the mean of D contributions.

@@ -1,0 +1,187 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every entry
+point include/zs.h declares, computes the unit layout like the oracle, and
+rejects invalid arguments before enqueuing anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+from oracle import zs_oracle as O
+
+import fsdp_sharded_optimizer_zs_amd as zs
+from fsdp_sharded_optimizer_zs_amd import _binding as B
+
+HEADER = os.path.join(ROOT, "include", "zs.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(zs_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from fsdp_sharded_optimizer_zs_amd import build
+        build.build()
+    return zs.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("zs_unit_layout", "zs_pack_flat", "zs_reduce_shard", "zs_adamw_step",
+              "zs_gather_unit", "zs_last_error", "zs_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    # nothing else of ours leaks out of the library
+    assert {e for e in exported if e.startswith("zs")} == set(declared_functions())
+
+
+def test_layout_matches_oracle(lib):
+    rng = np.random.default_rng(0)
+    for _ in range(300):
+        T = int(rng.integers(0, 12))
+        numels = [int(x) for x in rng.integers(0, 1000, size=T)]
+        if T and rng.random() < 0.3:
+            numels[int(rng.integers(0, T))] = 0
+        D = int(rng.integers(1, 65))
+        assert zs.zs_unit_layout(numels, D) == O.unit_layout(numels, D)
+
+
+def test_layout_workload_sizes(lib):
+    import workloads as W
+    for name in ("gpt3m", "llama7b_block"):
+        w = W.get(name)
+        assert zs.zs_unit_layout(w.units[0].numels, w.D) == O.unit_layout(w.units[0].numels, w.D)
+    big = [1 << 40] * 7 + [5]
+    assert zs.zs_unit_layout(big, 64) == O.unit_layout(big, 64)
+
+
+def test_layout_errors(lib):
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_unit_layout([3, -1], 4)
+    assert e.value.status == zs.ZS_EINVAL and "numels[1]" in zs.zs_last_error()
+    for D in (0, 65):
+        with pytest.raises(zs.ZsError):
+            zs.zs_unit_layout([3], D)
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_unit_layout([1 << 62, 1 << 62], 2)
+    assert e.value.status == zs.ZS_EUNSUPPORTED
+
+
+def _hp(**kw):
+    d = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+    d.update(kw)
+    return B.zs_adamw_hp(*[d[k] for k in ("lr", "beta1", "beta2", "eps", "weight_decay", "step")])
+
+
+def _adamw(lib, p, m, v, w, S, contribs, n, dtype, hp):
+    arr = (ctypes.c_void_p * max(1, len(contribs)))(*contribs)
+    return lib.zs_adamw_step(p, m, v, w, S, arr, n, dtype, ctypes.byref(hp) if hp else None, None)
+
+
+# Fake, never-dereferenced device addresses: every call below must fail in
+# host validation, before any HIP call. Where a GPU is visible these tests
+# are skipped, so that a validation gap can never launch a kernel on them.
+A = 0x7f0000000000
+
+
+def _no_gpu():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("fake-address validation tests run only where no GPU is visible")
+
+
+def test_adamw_argument_errors(lib):
+    _no_gpu()
+    S = 1024
+    p, m, v, w = A, A + 0x10000, A + 0x20000, A + 0x30000
+    c = [A + 0x40000]
+    assert _adamw(lib, p, m, v, w, S, c, 1, 7, _hp()) == zs.ZS_EUNSUPPORTED
+    assert _adamw(lib, p, m, v, w, S, c, 0, zs.ZS_BF16, _hp()) == zs.ZS_EINVAL
+    assert _adamw(lib, p, m, v, w, S, c * 65, 65, zs.ZS_BF16, _hp()) == zs.ZS_EINVAL
+    assert _adamw(lib, p, m, v, w, -1, c, 1, zs.ZS_BF16, _hp()) == zs.ZS_EINVAL
+    assert _adamw(lib, p, m, v, w, S, c, 1, zs.ZS_BF16, None) == zs.ZS_EINVAL
+    assert _adamw(lib, p, m, v, w, S, c, 1, zs.ZS_BF16, _hp(step=0)) == zs.ZS_EINVAL
+    assert "step" in zs.zs_last_error()
+    assert _adamw(lib, p, m, v, w, S, c, 1, zs.ZS_BF16, _hp(beta1=1.0)) == zs.ZS_EINVAL
+    assert _adamw(lib, p, m, v, w, S, c, 1, zs.ZS_BF16, _hp(beta2=-0.1)) == zs.ZS_EINVAL
+    assert _adamw(lib, p, m, v, w, S, c, 1, zs.ZS_BF16, _hp(lr=float("nan"))) == zs.ZS_EINVAL
+    assert _adamw(lib, p, m, v, w, S, c, 1, zs.ZS_BF16, _hp(eps=-1.0)) == zs.ZS_EINVAL
+    assert _adamw(lib, p, m, v, w, S, c, 1, zs.ZS_BF16, _hp(weight_decay=float("inf"))) == zs.ZS_EINVAL
+    assert _adamw(lib, 0, m, v, w, S, c, 1, zs.ZS_BF16, _hp()) == zs.ZS_EINVAL
+    assert _adamw(lib, p + 2, m, v, w, S, c, 1, zs.ZS_BF16, _hp()) == zs.ZS_EINVAL  # misaligned
+    assert _adamw(lib, p, m, v, w, S, [0], 1, zs.ZS_BF16, _hp()) == zs.ZS_EINVAL
+    assert _adamw(lib, p, m, v, w, S, [A + 0x40001], 1, zs.ZS_BF16, _hp()) == zs.ZS_EINVAL
+    # aliasing: p/m overlap, w inside v, a contribution over p
+    assert _adamw(lib, p, p + 4 * 100, v, w, S, c, 1, zs.ZS_BF16, _hp()) == zs.ZS_EALIAS
+    assert _adamw(lib, p, m, v, v + 8, S, c, 1, zs.ZS_BF16, _hp()) == zs.ZS_EALIAS
+    assert _adamw(lib, p, m, v, w, S, [p + 64], 1, zs.ZS_BF16, _hp()) == zs.ZS_EALIAS
+    assert "overlaps" in zs.zs_last_error()
+    # S == 0 is a no-op that succeeds without touching the device
+    assert _adamw(lib, p, m, v, w, 0, c, 1, zs.ZS_BF16, _hp()) == zs.ZS_OK
+    assert zs.zs_last_error() == ""
+
+
+def test_reduce_and_gather_argument_errors(lib):
+    _no_gpu()
+    arr = (ctypes.c_void_p * 2)(A, A + 0x10000)
+    assert lib.zs_reduce_shard(arr, 2, 9, 100, A + 0x20000, None) == zs.ZS_EUNSUPPORTED
+    assert lib.zs_reduce_shard(arr, 0, zs.ZS_BF16, 100, A + 0x20000, None) == zs.ZS_EINVAL
+    assert lib.zs_reduce_shard(arr, 2, zs.ZS_BF16, 100, None, None) == zs.ZS_EINVAL
+    assert lib.zs_reduce_shard(arr, 2, zs.ZS_BF16, 100, A + 0x10010, None) == zs.ZS_EALIAS
+    assert lib.zs_reduce_shard(None, 2, zs.ZS_BF16, 100, A + 0x20000, None) == zs.ZS_EINVAL
+    assert lib.zs_reduce_shard(arr, 2, zs.ZS_BF16, 0, None, None) == zs.ZS_OK
+    assert lib.zs_gather_unit(arr, 2, 100, zs.ZS_BF16, A + 0x80, None) == zs.ZS_EALIAS
+    assert lib.zs_gather_unit(arr, 2, 100, zs.ZS_BF16, None, None) == zs.ZS_EINVAL
+    assert lib.zs_gather_unit(arr, 2, 100, zs.ZS_F32, A + 0x20001, None) == zs.ZS_EINVAL
+    assert lib.zs_gather_unit(arr, 65, 100, zs.ZS_BF16, A + 0x20000, None) == zs.ZS_EINVAL
+    assert lib.zs_gather_unit(arr, 2, 1 << 62, zs.ZS_BF16, A + 0x20000, None) == zs.ZS_EINVAL
+
+
+def test_pack_argument_errors(lib):
+    _no_gpu()
+    T = 3
+    h = (B.zs_tensor_ref * T)(B.zs_tensor_ref(A, 10, 0), B.zs_tensor_ref(A + 0x1000, 5, 10),
+                               B.zs_tensor_ref(A + 0x2000, 1, 15))
+    sh = (ctypes.c_void_p * 4)(A + 0x10000, A + 0x11000, A + 0x12000, A + 0x13000)
+    dt = A + 0x30000
+    assert lib.zs_pack_flat(h, dt, T, zs.ZS_BF16, 4, sh, 3, None) == zs.ZS_EINVAL     # S != 4
+    assert "ceil(N/D)" in zs.zs_last_error()
+    h[1].flat_offset = 11
+    assert lib.zs_pack_flat(h, dt, T, zs.ZS_BF16, 4, sh, 4, None) == zs.ZS_EINVAL
+    h[1].flat_offset = 10
+    h[2].ptr = A + 0x2001
+    assert lib.zs_pack_flat(h, dt, T, zs.ZS_BF16, 4, sh, 4, None) == zs.ZS_EINVAL     # misaligned
+    h[2].ptr = A + 0x2000
+    sh[1] = A + 0x10004
+    assert lib.zs_pack_flat(h, dt, T, zs.ZS_BF16, 4, sh, 4, None) == zs.ZS_EALIAS     # shards overlap
+    sh[1] = A + 0x1002
+    assert lib.zs_pack_flat(h, dt, T, zs.ZS_BF16, 4, sh, 4, None) == zs.ZS_EALIAS     # shard over tensor
+    sh[1] = A + 0x11000
+    assert lib.zs_pack_flat(h, None, T, zs.ZS_BF16, 4, sh, 4, None) == zs.ZS_EINVAL
+    assert lib.zs_pack_flat(h, dt, T, 3, 4, sh, 4, None) == zs.ZS_EUNSUPPORTED
+    h0 = (B.zs_tensor_ref * 1)(B.zs_tensor_ref(None, 0, 0))
+    assert lib.zs_pack_flat(h0, dt, 1, zs.ZS_F32, 4, sh, 0, None) == zs.ZS_OK          # N = 0
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    x = torch.zeros(16)
+    with pytest.raises(ValueError):
+        zs.zs_reduce_shard([x.to(torch.bfloat16)], x)
+    with pytest.raises(ValueError):
+        zs.zs_adamw_step(x, x.clone(), x.clone(), torch.zeros(16, dtype=torch.int16), [x], B.AdamWHP(1e-3, 0.9, 0.95, 1e-8, 0.0, 1))

@@ -148,3 +148,17 @@ def test_rank_shard_lengths_multi_unit():
     assert sum(S) == 8_622_081_024
     w = W.get("llama7b_full")
     assert sum(O.unit_layout(u.numels, w.D)[3] for u in w.units) == 210_575_488
+
+
+def test_flat_source_against_pack():
+    rng = np.random.default_rng(9)
+    for _ in range(30):
+        numels = [int(x) for x in rng.integers(0, 40, size=rng.integers(1, 8))]
+        D = int(rng.integers(1, 9))
+        offsets, N, N_pad, S = O.unit_layout(numels, D)
+        ts = labelled_tensors(numels)
+        flat = np.concatenate(O.pack_flat(ts, D)) if N_pad else np.zeros(0, np.uint16)
+        j, e = O.flat_source(offsets, np.arange(N_pad))
+        for i in range(N_pad):
+            want = 0 if j[i] < 0 else int(ts[j[i]][e[i]])
+            assert int(flat[i]) == want
