@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "params/s and achieved HBM GB/s (% of peak) for fused reduce+AdamW shard step"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 CONTRIB_POOL = 4
-PMC_FILE = os.path.join(ROOT, "profiles", "adamw_fused_llama70b_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "adamw_fused_llama70b_hbm_counters.md")
 KERNEL_SRC = os.path.join(ROOT, "fsdp_sharded_optimizer_zs_amd", "csrc", "zs_step.hip")
 
 
@@ -51,17 +51,26 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(bytes_per_launch_alg: float):
-    """Measured HBM bytes per launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+def traffic_from_profiles():
+    """Measured HBM bytes per launch of the fused kernel, from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source;
+    else None. The summary holds `key: value` lines in a fenced block."""
     try:
         with open(PMC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            text = f.read()
+    except OSError:
         return None
+    rec = {}
+    for line in text.splitlines():
+        k, sep, val = line.partition(":")
+        if sep and k.strip() in ("kernel_src_sha256_16", "hbm_bytes_per_launch"):
+            rec[k.strip()] = val.strip()
     if rec.get("kernel_src_sha256_16") != kernel_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(p, m, v, contribs, t: int, hp: dict):
@@ -85,8 +94,8 @@ def cpu_baseline(p, m, v, contribs, t: int, hp: dict):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run a plain 4 GiB device copy (HBM counter calibration)")
@@ -195,7 +204,7 @@ def main() -> int:
     bytes_per_launch = bpp * S / n_launch
     achieved = bytes_per_launch / adam_avg_s / 1e9
     gather_bytes = 4.0 * D * S                     # D*S bf16 read + written per step
-    traffic = traffic_from_profiles(bytes_per_launch)
+    traffic = traffic_from_profiles()
     out = {
         "metric": METRIC,
         "value": S * K / elapsed,
@@ -220,6 +229,8 @@ def main() -> int:
             "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
+            "traffic_over_algorithmic": (traffic / bytes_per_launch) if traffic else None,
             "algorithmic_bytes_per_param": bpp,
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "avg_launch_ms": adam_avg_s * 1e3,

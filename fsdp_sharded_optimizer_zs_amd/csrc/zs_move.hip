@@ -11,8 +11,11 @@
 
 #include "zs_internal.h"
 
-#ifndef ZS_BLOCKS_PER_CU
-#define ZS_BLOCKS_PER_CU 8
+// Workgroups (of 4 wavefronts) per CU for the copies: 4 per CU moved the
+// 70B block unit's gather at 5.56 TB/s on MI355X, against 5.26 TB/s with 8
+// and 5.12 TB/s with 2.
+#ifndef ZS_MOVE_BLOCKS_PER_CU
+#define ZS_MOVE_BLOCKS_PER_CU 4
 #endif
 
 namespace zs {
@@ -132,7 +135,7 @@ hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es, i
                        const PtrPack& shards, int64_t S, hipStream_t stream) {
     const int64_t per_shard = (S + kPackChunk - 1) / kPackChunk;
     const int64_t items = per_shard * D;
-    int64_t blocks = int64_t(device_info().cu_count) * ZS_BLOCKS_PER_CU;
+    int64_t blocks = int64_t(device_info().cu_count) * ZS_MOVE_BLOCKS_PER_CU;
     if (blocks > items) blocks = items;
     if (blocks < 1) blocks = 1;
     if (es == 2)
@@ -148,7 +151,7 @@ hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es, void* 
                          hipStream_t stream) {
     const int64_t vecs = (S * es + 15) / 16 + 1;
     int64_t bx = (vecs + kThreads - 1) / kThreads;
-    const int64_t cap = (int64_t(device_info().cu_count) * ZS_BLOCKS_PER_CU + D - 1) / D;
+    const int64_t cap = (int64_t(device_info().cu_count) * ZS_MOVE_BLOCKS_PER_CU + D - 1) / D;
     if (bx > cap) bx = cap;
     if (bx < 1) bx = 1;
     char* f = static_cast<char*>(flat);
