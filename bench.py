@@ -91,12 +91,70 @@ def cpu_baseline(p, m, v, contribs, t: int, hp: dict):
     return n / dt, dt, n
 
 
+def pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D, step_t, hp, host_buckets):
+    """Per-bucket streamed step: contributions copied into two alternating
+    staging slots on a transfer stream while the fused step of the previous
+    bucket runs on the compute stream (zs_step_pipelined). For device and
+    pinned-host sources, times the copies alone, the steps alone (sources
+    already resident) and the pipelined form, and reports how much of the
+    shorter phase the overlap hid: (copy + compute - pipelined) / min(...)."""
+    dev = p.device
+    bmax = pool.shape[2]
+    staging = (torch.empty((D, bmax), dtype=torch.int16, device=dev),
+               torch.empty((D, bmax), dtype=torch.int16, device=dev))
+    compute = torch.cuda.Stream(device=dev)
+    transfer = torch.cuda.Stream(device=dev)
+    res = {}
+    for kind, nb in (("device_sources", len(buckets)), ("pinned_host_sources", host_buckets)):
+        if kind == "device_sources":
+            srcs = [[pool[b % pool.shape[0], k, :sz] for k in range(D)]
+                    for b, (_, sz, _, _, _) in enumerate(buckets[:nb])]
+        else:
+            hpool = torch.empty((2, D, bmax), dtype=torch.int16, pin_memory=True)
+            hpool.copy_(pool[:2])
+            srcs = [[hpool[b % 2, k, :sz] for k in range(D)]
+                    for b, (_, sz, _, _, _) in enumerate(buckets[:nb])]
+        bl = [(p[sl], m[sl], v[sl], wshard[sl], srcs[b])
+              for b, (sl, sz, _, _, _) in enumerate(buckets[:nb])]
+        h = dict(step=step_t, **hp)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(transfer):           # copies alone
+            e[0].record()
+            for b, (_, sz, _, _, _) in enumerate(buckets[:nb]):
+                for k in range(D):
+                    staging[b & 1][k, :sz].copy_(srcs[b][k], non_blocking=True)
+            e[1].record()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(compute):            # steps alone, sources resident
+            e[2].record()
+            for b, (sl, sz, cs, _, _) in enumerate(buckets[:nb]):
+                zs.zs_adamw_step(p[sl], m[sl], v[sl], wshard[sl], cs, zs.AdamWHP(**h))
+            e[3].record()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(compute):            # pipelined
+            e[4].record()
+            zs.zs_step_pipelined(bl, staging, h, compute, transfer)
+            e[5].record()
+        torch.cuda.synchronize()
+        tc, tk, tp = e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3]), e[4].elapsed_time(e[5])
+        moved = sum(D * 2 * sz for (_, sz, _, _, _) in buckets[:nb])
+        res[kind] = {"buckets": nb, "copy_ms": tc, "copy_GB_s": moved / (tc / 1e3) / 1e9,
+                     "step_ms": tk, "pipelined_ms": tp,
+                     "serial_ms": tc + tk,
+                     "overlap_hidden_frac": (tc + tk - tp) / min(tc, tk)}
+        del srcs, bl
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="skip the per-bucket streamed (overlapped) step leg")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run a plain 4 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -255,11 +313,15 @@ def main() -> int:
         out["copy_4GiB"] = {"ms": c0.elapsed_time(c1),
                             "GB_s": 2 * 4 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9}
         del a, bb
+    if not args.no_pipeline:
+        log("pipeline leg: contributions streamed per bucket, overlapped with the step")
+        out["pipeline"] = pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D,
+                                       args.warmup + K + 1, hp, host_buckets=16)
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on one block bucket (host copies)")
         sl, sz, cs, _, _ = buckets[0]
         # one step of the oracle from the bucket's current state
-        rate, secs, n = cpu_baseline(p[sl], m[sl], v[sl], cs, args.warmup + K + 1, hp)
+        rate, secs, n = cpu_baseline(p[sl], m[sl], v[sl], cs, args.warmup + K + 2, hp)
         out["cpu_baseline"] = {
             "value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"one block bucket of the same workload ({n} params, D=8 bf16 "

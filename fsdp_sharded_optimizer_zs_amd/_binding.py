@@ -34,6 +34,12 @@ class zs_tensor_ref(ctypes.Structure):
                 ("flat_offset", ctypes.c_int64)]
 
 
+class zs_bucket(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("w_out", ctypes.c_void_p), ("S", ctypes.c_int64),
+                ("sources", ctypes.POINTER(ctypes.c_void_p))]
+
+
 class zs_adamw_hp(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
@@ -73,6 +79,8 @@ def load() -> ctypes.CDLL:
                 "zs_adamw_step": (i32, [vp, vp, vp, vp, i64, P(vp), i32, i32,
                                         P(zs_adamw_hp), vp]),
                 "zs_gather_unit": (i32, [P(vp), i32, i64, i32, vp, vp]),
+                "zs_step_pipelined": (i32, [P(zs_bucket), i32, i32, i32, vp, vp, i64,
+                                            P(zs_adamw_hp), vp, vp]),
                 "zs_last_error": (ctypes.c_char_p, []),
                 "zs_abi_version": (i32, []),
             }
@@ -236,6 +244,52 @@ def zs_gather_unit(shards: Sequence, flat_out, stream=None) -> None:
         raise ValueError(f"flat_out must hold D*S = {D * S} elements")
     _check(load().zs_gather_unit(_ptr_array(shards), D, S, code,
                                  ctypes.c_void_p(flat_out.data_ptr()), _stream(flat_out, stream)))
+
+
+def zs_step_pipelined(buckets: Sequence, staging: Sequence, hp, compute=None,
+                      transfer=None) -> None:
+    """The shard step over buckets [(p, m, v, w_out, sources), ...], each
+    bucket's sources (device tensors or pinned host tensors, one dtype)
+    copied into alternating staging slots on `transfer` while the previous
+    bucket steps on `compute`. staging = (slot0, slot1): device tensors of
+    the sources' dtype, shape [n_contrib, staging_len]."""
+    torch = _torch()
+    if len(staging) != 2:
+        raise ValueError("staging must be two slot tensors")
+    s0, s1 = staging
+    for i, t in enumerate((s0, s1)):
+        _dev(t, f"staging[{i}]")
+        if t.dim() != 2 or t.shape != s0.shape or t.dtype != s0.dtype:
+            raise ValueError("staging slots must be equal [n_contrib, staging_len] tensors")
+    n_contrib, staging_len = int(s0.shape[0]), int(s0.shape[1])
+    code = _dtype_code(s0)
+    arr = (zs_bucket * max(1, len(buckets)))()
+    keep = []
+    for b, (p, m, v, w, srcs) in enumerate(buckets):
+        S = p.numel()
+        for name, t in (("p", p), ("m", m), ("v", v)):
+            _dev(t, f"bucket {b} {name}")
+            if t.dtype != torch.float32 or t.numel() != S:
+                raise ValueError(f"bucket {b}: {name} must be float32 with S = {S} elements")
+        _dev(w, f"bucket {b} w_out")
+        if _dtype_code(w) != ZS_BF16 or w.numel() != S:
+            raise ValueError(f"bucket {b}: w_out must be bf16 bits with S elements")
+        if len(srcs) != n_contrib:
+            raise ValueError(f"bucket {b}: need {n_contrib} sources")
+        for q, c in enumerate(srcs):
+            if not c.is_contiguous() or c.numel() != S or _dtype_code(c) != code:
+                raise ValueError(f"bucket {b} source {q}: contiguous, S elements, staging dtype")
+            if not c.is_cuda and c.numel() > 0 and not c.is_pinned():
+                raise ValueError(f"bucket {b} source {q}: host sources must be pinned memory")
+        ptrs = _ptr_array(srcs)
+        keep.append(ptrs)
+        arr[b] = zs_bucket(p.data_ptr(), m.data_ptr(), v.data_ptr(), w.data_ptr(), S,
+                           ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)))
+    h = _hp(hp)
+    _check(load().zs_step_pipelined(arr, len(buckets), n_contrib, code,
+                                    ctypes.c_void_p(s0.data_ptr()), ctypes.c_void_p(s1.data_ptr()),
+                                    staging_len, ctypes.byref(h), _stream(s0, compute),
+                                    _stream(s0, transfer)))
 
 
 # Raw-pointer forms, for callers that manage device memory themselves.

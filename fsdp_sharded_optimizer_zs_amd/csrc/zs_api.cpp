@@ -16,8 +16,8 @@
 
 namespace zs {
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
 zs_status fail(zs_status code, const char* fmt, ...) {
     char buf[512];
@@ -44,11 +44,6 @@ int elem_size(int32_t dtype) {
     if (dtype == ZS_F32) return 4;
     return 0;
 }
-
-// Byte range [lo, hi) of a buffer, for overlap checks.
-struct Range {
-    uintptr_t lo, hi;
-};
 
 Range range_of(const void* p, int64_t count, int es) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
@@ -77,7 +72,42 @@ zs_status take_ptrs(const void* const* src, int n, int es, const char* what, Ptr
     return ZS_OK;
 }
 
-}  // namespace
+zs_status check_hp(const zs_adamw_hp* hp, const char* who) {
+    if (hp == nullptr) return fail(ZS_EINVAL, "%s: hp is NULL", who);
+    if (hp->step < 1) return fail(ZS_EINVAL, "%s: step = %lld < 1", who, (long long)hp->step);
+    if (!(std::isfinite(hp->lr) && hp->lr >= 0.0))
+        return fail(ZS_EINVAL, "%s: lr must be finite and >= 0", who);
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+        return fail(ZS_EINVAL, "%s: betas must lie in [0, 1)", who);
+    if (!(std::isfinite(hp->eps) && hp->eps >= 0.0))
+        return fail(ZS_EINVAL, "%s: eps must be finite and >= 0", who);
+    if (!(std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.0))
+        return fail(ZS_EINVAL, "%s: weight_decay must be finite and >= 0", who);
+    return ZS_OK;
+}
+
+AdamConsts adam_consts(const zs_adamw_hp& hp, int n_contrib) {
+    // Double arithmetic, each constant rounded to fp32 once.
+    double b1t = 1.0, b2t = 1.0;
+    for (int64_t t = 0; t < hp.step; ++t) {
+        b1t = b1t * hp.beta1;
+        b2t = b2t * hp.beta2;
+        // Below 2^-54, 1 - b rounds to exactly 1.0 in double, so more
+        // factors cannot change any constant derived from b1t or b2t.
+        if (b1t < 0x1p-54 && b2t < 0x1p-54) break;
+    }
+    AdamConsts k;
+    k.dec = float(1.0 - hp.lr * hp.weight_decay);
+    k.b1 = float(hp.beta1);
+    k.b1c = float(1.0 - hp.beta1);
+    k.b2 = float(hp.beta2);
+    k.b2c = float(1.0 - hp.beta2);
+    k.ss = float(hp.lr / (1.0 - b1t));
+    k.bc2s = float(std::sqrt(1.0 - b2t));
+    k.eps = float(hp.eps);
+    k.inv_n = float(1.0 / double(n_contrib));
+    return k;
+}
 
 const DeviceInfo& device_info() {
     static std::mutex mu;
@@ -103,7 +133,7 @@ using namespace zs;
 
 ZS_EXPORT const char* zs_last_error(void) { return g_last_error.c_str(); }
 
-ZS_EXPORT int32_t zs_abi_version(void) { return 100; }
+ZS_EXPORT int32_t zs_abi_version(void) { return 101; }
 
 ZS_EXPORT zs_status zs_unit_layout(const int64_t* numels, int32_t T, int32_t D,
                                    int64_t* offsets_out, int64_t* n_out, int64_t* n_pad_out,
@@ -213,22 +243,14 @@ ZS_EXPORT zs_status zs_adamw_step(float* p, float* m, float* v, uint16_t* w_out,
     if (n_contrib < 1 || n_contrib > ZS_MAX_D)
         return fail(ZS_EINVAL, "zs_adamw_step: n_contrib = %d outside 1..%d", n_contrib, ZS_MAX_D);
     if (!size_ok(S, 4)) return fail(ZS_EINVAL, "zs_adamw_step: S = %lld out of range", (long long)S);
-    if (hp == nullptr) return fail(ZS_EINVAL, "zs_adamw_step: hp is NULL");
-    if (hp->step < 1) return fail(ZS_EINVAL, "zs_adamw_step: step = %lld < 1", (long long)hp->step);
-    if (!(std::isfinite(hp->lr) && hp->lr >= 0.0))
-        return fail(ZS_EINVAL, "zs_adamw_step: lr must be finite and >= 0");
-    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
-        return fail(ZS_EINVAL, "zs_adamw_step: betas must lie in [0, 1)");
-    if (!(std::isfinite(hp->eps) && hp->eps >= 0.0))
-        return fail(ZS_EINVAL, "zs_adamw_step: eps must be finite and >= 0");
-    if (!(std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.0))
-        return fail(ZS_EINVAL, "zs_adamw_step: weight_decay must be finite and >= 0");
+    zs_status st = check_hp(hp, "zs_adamw_step");
+    if (st != ZS_OK) return st;
     if (S == 0) return ok();
     if (!p || !m || !v || !w_out) return fail(ZS_EINVAL, "zs_adamw_step: p, m, v or w_out is NULL");
     if (!aligned(p, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(w_out, 2))
         return fail(ZS_EINVAL, "zs_adamw_step: p, m, v or w_out misaligned for its element type");
     PtrPack cp;
-    zs_status st = take_ptrs(contribs, n_contrib, es, "zs_adamw_step: contribs", &cp);
+    st = take_ptrs(contribs, n_contrib, es, "zs_adamw_step: contribs", &cp);
     if (st != ZS_OK) return st;
     const Range rs[4] = {range_of(p, S, 4), range_of(m, S, 4), range_of(v, S, 4),
                          range_of(w_out, S, 2)};
@@ -246,25 +268,7 @@ ZS_EXPORT zs_status zs_adamw_step(float* p, float* m, float* v, uint16_t* w_out,
         al = al && aligned(cp.p[k], 16);
     }
 
-    // Constants: double arithmetic, each rounded to fp32 once.
-    double b1t = 1.0, b2t = 1.0;
-    for (int64_t t = 0; t < hp->step; ++t) {
-        b1t = b1t * hp->beta1;
-        b2t = b2t * hp->beta2;
-        // Below 2^-54, 1 - b rounds to exactly 1.0 in double, so more
-        // factors cannot change any constant derived from b1t or b2t.
-        if (b1t < 0x1p-54 && b2t < 0x1p-54) break;
-    }
-    AdamConsts k;
-    k.dec = float(1.0 - hp->lr * hp->weight_decay);
-    k.b1 = float(hp->beta1);
-    k.b1c = float(1.0 - hp->beta1);
-    k.b2 = float(hp->beta2);
-    k.b2c = float(1.0 - hp->beta2);
-    k.ss = float(hp->lr / (1.0 - b1t));
-    k.bc2s = float(std::sqrt(1.0 - b2t));
-    k.eps = float(hp->eps);
-    k.inv_n = float(1.0 / double(n_contrib));
+    const AdamConsts k = adam_consts(*hp, n_contrib);
     return hip_status(launch_adamw(p, m, v, w_out, S, cp, n_contrib, dtype, k, al, stream),
                       "zs_adamw_step launch");
 }

@@ -27,6 +27,22 @@ struct AdamConsts {
     float inv_n;  // 1 / n_contrib
 };
 
+// Host-side helpers shared by the entry points (zs_api.cpp).
+zs_status fail(zs_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+zs_status ok();  // clears the calling thread's error text
+zs_status hip_status(hipError_t e, const char* what);
+int elem_size(int32_t dtype);  // 2, 4, or 0 for an unknown tag
+struct Range {                 // byte range [lo, hi) of a buffer
+    uintptr_t lo, hi;
+};
+Range range_of(const void* p, int64_t count, int es);
+bool overlap(const Range& a, const Range& b);
+bool aligned(const void* p, uintptr_t a);
+bool size_ok(int64_t S, int es);
+zs_status take_ptrs(const void* const* src, int n, int es, const char* what, PtrPack* out);
+zs_status check_hp(const zs_adamw_hp* hp, const char* who);
+AdamConsts adam_consts(const zs_adamw_hp& hp, int n_contrib);
+
 // Launch geometry of the device the caller's stream runs on.
 struct DeviceInfo {
     int cu_count;

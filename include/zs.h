@@ -9,6 +9,8 @@
  *   zs_reduce_shard  reduce-scatter arithmetic for one shard
  *   zs_adamw_step    fused reduce + mixed-precision AdamW on one shard
  *   zs_gather_unit   all-gather's local rebuild of a unit from its shards
+ *   zs_step_pipelined  the step over a sequence of buckets, each bucket's
+ *                    contribution transfer overlapped with the previous step
  *
  * Sources (web pages, by title and section):
  *   [ZT]   "7.10 -- Fully-sharded data parallel (FSDP / ZeRO-3)", AI / ML
@@ -203,6 +205,59 @@ zs_status zs_adamw_step(float* p, float* m, float* v, uint16_t* w_out, int64_t S
  */
 zs_status zs_gather_unit(const void* const* shards, int32_t D, int64_t S,
                          int32_t dtype, void* flat_out, hipStream_t stream);
+
+/* One bucket of a rank's shard (one FSDP unit's slice) for the pipelined step. */
+typedef struct {
+    float* p;                    /* device, S floats: fp32 master, updated in place */
+    float* m;                    /* device, S floats: first moment, in place        */
+    float* v;                    /* device, S floats: second moment, in place       */
+    uint16_t* w_out;             /* device, S bf16: working shard, written          */
+    int64_t S;                   /* >= 0; 0 skips the bucket                        */
+    const void* const* sources;  /* host array of n_contrib pointers, each to S
+                                    elements of the reduce dtype, in device memory
+                                    or pinned host memory; read only            */
+} zs_bucket;
+
+/*
+ * zs_step_pipelined -- the shard step over a sequence of buckets, with the
+ * arrival of each bucket's contributions overlapped with the previous
+ * bucket's fused step.
+ *
+ * [ZT] section 5.4 and [GPT8] "Prefetching: Hiding the Cost": FSDP issues
+ * the collective of the next block while the current block computes, so
+ * communication hides behind compute. Here the reduce-scatter's transfer is
+ * stood in for by copies of the n_contrib contributions of bucket b from
+ * `sources` into a device staging slot (slots alternate between staging0
+ * and staging1), enqueued on `transfer`; the fused step of bucket b (the
+ * exact arithmetic of zs_adamw_step with these contributions) runs on
+ * `compute` once its copies have landed, and the copies of the bucket after
+ * next wait until that step has released the slot. The first copies wait
+ * for all work already enqueued on `compute`. Results are bit-identical to
+ * calling zs_adamw_step on every bucket in order.
+ *
+ *   buckets      host array of n_buckets bucket descriptors
+ *   n_buckets    >= 0
+ *   n_contrib    1..ZS_MAX_D contributions per bucket
+ *   dtype        ZS_BF16 or ZS_F32: element type of sources and staging
+ *   staging0/1   device, n_contrib * staging_len elements each; contribution
+ *                q of a bucket lands at element q * staging_len of its slot
+ *   staging_len  >= every bucket's S (a multiple of 8 keeps the full-speed
+ *                kernel)
+ *   hp           host pointer to the hyperparameters (one step for all buckets)
+ *   compute      stream that runs the steps; when all work enqueued on it by
+ *                this call has completed, every copy has completed too
+ *   transfer     stream that runs the copies (may equal compute: no overlap)
+ * Returns after enqueuing; nothing is synchronized and no device memory is
+ * allocated (five events are created and released per call).
+ * Errors: ZS_EINVAL (NULLs, misalignment, a bucket larger than staging_len,
+ * hyperparameters), ZS_EALIAS (any two of the buckets' p, m, v, w_out and the
+ * staging slots overlap, or a source overlaps one of them), ZS_EUNSUPPORTED,
+ * ZS_EHIP (a runtime call failed; buckets before the failing one may already
+ * be enqueued).
+ */
+zs_status zs_step_pipelined(const zs_bucket* buckets, int32_t n_buckets, int32_t n_contrib,
+                            int32_t dtype, void* staging0, void* staging1, int64_t staging_len,
+                            const zs_adamw_hp* hp, hipStream_t compute, hipStream_t transfer);
 
 /* Text of the calling thread's most recent failure ("" if none). The pointer
  * stays valid until the thread's next call into the library. */

@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("zs_unit_layout", "zs_pack_flat", "zs_reduce_shard", "zs_adamw_step",
-              "zs_gather_unit", "zs_last_error", "zs_abi_version"):
+              "zs_gather_unit", "zs_step_pipelined", "zs_last_error", "zs_abi_version"):
         assert n in names
 
 
@@ -185,3 +185,49 @@ def test_binding_refuses_host_tensors(lib):
         zs.zs_reduce_shard([x.to(torch.bfloat16)], x)
     with pytest.raises(ValueError):
         zs.zs_adamw_step(x, x.clone(), x.clone(), torch.zeros(16, dtype=torch.int16), [x], B.AdamWHP(1e-3, 0.9, 0.95, 1e-8, 0.0, 1))
+
+
+def _bucket(p, S, srcs):
+    arr = (ctypes.c_void_p * len(srcs))(*srcs)
+    b = B.zs_bucket(p, p + 0x100000, p + 0x200000, p + 0x300000, S,
+                    ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)))
+    return b, arr
+
+
+def test_pipelined_argument_errors(lib):
+    _no_gpu()
+    f = lib.zs_step_pipelined
+    s0, s1 = A + 0x10000000, A + 0x11000000
+    b0, k0 = _bucket(A, 1000, [A + 0x20000000, A + 0x20100000])
+    b1, k1 = _bucket(A + 0x1000000, 900, [A + 0x20200000, A + 0x20300000])
+    arr = (B.zs_bucket * 2)(b0, b1)
+    hp = _hp()
+    run = lambda a=arr, n=2, nc=2, dt=zs.ZS_BF16, x=s0, y=s1, L=1000, h=hp: f(
+        a, n, nc, dt, x, y, L, ctypes.byref(h) if h is not None else None, None, None)
+    assert run(dt=5) == zs.ZS_EUNSUPPORTED
+    assert run(nc=0) == zs.ZS_EINVAL
+    assert run(n=-1) == zs.ZS_EINVAL
+    assert run(h=None) == zs.ZS_EINVAL
+    assert run(h=_hp(step=0)) == zs.ZS_EINVAL
+    assert run(n=0) == zs.ZS_OK                         # nothing to do, no HIP call
+    assert run(L=999) == zs.ZS_EINVAL                   # bucket 0 larger than a slot
+    assert "staging_len" in zs.zs_last_error()
+    assert run(x=None) == zs.ZS_EINVAL
+    assert run(x=s0 + 1) == zs.ZS_EINVAL                # misaligned slot
+    assert run(y=s0 + 2 * 1000) == zs.ZS_EALIAS         # slot 1 inside slot 0 (2 x 1000 bf16)
+    arr[1].p = A + 0x40                                 # bucket 1's p overlaps bucket 0's p
+    assert run() == zs.ZS_EALIAS
+    arr[1].p = A + 0x1000000
+    k1[0] = s1 + 64                                     # a source inside staging slot 1
+    assert run() == zs.ZS_EALIAS
+    k1[0] = A + 0x20200000
+    k1[1] = A + 0x300000 + 16                           # a source over bucket 0's w_out
+    assert run() == zs.ZS_EALIAS
+    k1[1] = 0
+    assert run() == zs.ZS_EINVAL                        # NULL source
+    k1[1] = A + 0x20300000
+    arr[0].p = 0
+    assert run() == zs.ZS_EINVAL
+    arr[0].p = A
+    arr[0].S = -5
+    assert run() == zs.ZS_EINVAL
