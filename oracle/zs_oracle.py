@@ -170,6 +170,62 @@ def reduce_shard(contribs: Sequence[np.ndarray], dtype: str) -> np.ndarray:
     return (s * inv_d).astype(F32)
 
 
+def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    """The value a float32 result takes once stored in the reduce dtype:
+    bf16 rounds to nearest even (bf16_round) and widens back exactly; fp32
+    is unchanged."""
+    x = np.asarray(x, dtype=F32)
+    if dtype == BF16:
+        return bf16_widen(bf16_round(x))
+    if dtype == FP32:
+        return x.copy()
+    raise ValueError(dtype)
+
+
+def reduce_shard_hybrid(contribs: Sequence[np.ndarray], dtype: str, replicas: int,
+                        round_to_reduce_dtype: bool) -> np.ndarray:
+    """Reduce-scatter arithmetic under HYBRID_SHARD, optionally rounding
+    each collective's output to the reduce dtype.
+
+    [GPT8 "Sharding Strategies", "HYBRID_SHARD: The Multi-Node Strategy"]:
+    parameters are fully sharded across the D GPUs of a node and replicated
+    across the R nodes; a node reduce-scatters its gradients over its local
+    ranks, and the nodes then combine their shards with one all-reduce per
+    step. [RP 2] and [GPT8 "Mixed Precision"] name the dtype the collectives
+    communicate in (bf16 or fp32). Reading taken: contributions are ordered
+    replica-major (contribs[j*D + k] is local rank k of node j). Node j's
+    partial sum s_j is the left fold of its D widened contributions in fp32;
+    when the collectives' outputs are held in the reduce dtype, s_j is
+    rounded to it. The nodes' partial sums are folded left in node order in
+    fp32 and, again when rounding, rounded to the reduce dtype. The mean is
+    one multiply by float32(1/(R*D)); the result stays fp32. With R = 1 and
+    no rounding this is reduce_shard exactly.
+    """
+    n = len(contribs)
+    if replicas < 1 or n < 1 or n % replicas:
+        raise ValueError("need R >= 1 groups of D >= 1 contributions")
+    D = n // replicas
+
+    def widen(c):
+        if dtype == BF16:
+            return bf16_widen(c)
+        if dtype == FP32:
+            return np.asarray(c, dtype=F32)
+        raise ValueError(dtype)
+
+    total = None
+    for j in range(replicas):
+        s = widen(contribs[j * D]).copy()
+        for k in range(1, D):
+            s = (s + widen(contribs[j * D + k])).astype(F32)
+        if round_to_reduce_dtype:
+            s = round_to_dtype(s, dtype)
+        total = s if total is None else (total + s).astype(F32)
+    if round_to_reduce_dtype:
+        total = round_to_dtype(total, dtype)
+    return (total * F32(1.0 / n)).astype(F32)
+
+
 # --------------------------------------------------------------- O4: AdamW
 @dataclasses.dataclass(frozen=True)
 class AdamWHP:
@@ -252,6 +308,14 @@ def rank_step(p, m, v, contribs: Sequence[np.ndarray], dtype: str, hp: AdamWHP):
     the local shard. Returns (p, m, v, w).
     """
     g = reduce_shard(contribs, dtype)
+    return adamw_step(p, m, v, g, hp)
+
+
+def rank_step_hybrid(p, m, v, contribs: Sequence[np.ndarray], dtype: str, hp: AdamWHP,
+                     replicas: int, round_to_reduce_dtype: bool):
+    """The rank's shard step with the HYBRID_SHARD / reduce-dtype reduce of
+    reduce_shard_hybrid, then AdamW (O4). Returns (p, m, v, w)."""
+    g = reduce_shard_hybrid(contribs, dtype, replicas, round_to_reduce_dtype)
     return adamw_step(p, m, v, g, hp)
 
 
