@@ -147,12 +147,107 @@ def pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D, step_t, hp, host_
     return res
 
 
+def hybrid_leg(zs, torch, W, dev, hp, steps: int):
+    """HYBRID_SHARD shard step on the full LLaMA-7B rank shard of a 4-node x
+    8-GPU job (D = 8 per node, 4 replica groups, bf16 collectives): one
+    zs_adamw_step_ex per unit bucket (33), 32 bf16 contributions each. The
+    same buckets are also stepped with the flat 32-contribution reduce
+    (zs_adamw_step), which moves the same 26 + 32 * 2 = 90 B/param."""
+    w = W.get("llama7b_hybrid")
+    R, D = w.replicas, w.D
+    sizes = [zs.zs_unit_layout(u.numels, D)[3] for u in w.units]
+    S = int(sum(sizes))
+    bmax = max(sizes)
+    p = W.master_init(S, 6000, dev)
+    m = torch.zeros(S, device=dev)
+    v = torch.zeros(S, device=dev)
+    ws = torch.empty(S, dtype=torch.int16, device=dev)
+    pool = torch.empty((2, R * D, bmax), dtype=torch.int16, device=dev)
+    for s_ in range(2):
+        for k in range(R * D):
+            pool[s_, k].copy_(W.contribution(w, bmax, 1, s_, k, dev))
+    off = 0
+    bl = []
+    for b, sz in enumerate(sizes):
+        bl.append((slice(off, off + sz), [pool[b % 2, k, :sz] for k in range(R * D)]))
+        off += sz
+    torch.cuda.synchronize()
+
+    def run(t, hybrid):
+        h = dict(step=t, **hp)
+        for sl, cs in bl:
+            if hybrid:
+                zs.zs_adamw_step_ex(p[sl], m[sl], v[sl], ws[sl], cs, h, replicas=R,
+                                    round_to_reduce_dtype=w.round_reduce)
+            else:
+                zs.zs_adamw_step(p[sl], m[sl], v[sl], ws[sl], cs, h)
+
+    res = {"workload": w.description, "shard_params": S, "buckets": len(sizes),
+           "replicas": R, "D": D, "algorithmic_bytes_per_param": 26 + R * D * 2}
+    for name, hybrid in (("hybrid", True), ("flat32", False)):
+        run(1, hybrid)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for t in range(2, 2 + steps):
+            run(t, hybrid)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name] = {"ms_per_step": ms, "params_per_s": S / (ms / 1e3),
+                     "GB_s": (26 + R * D * 2) * S / (ms / 1e3) / 1e9}
+    del p, m, v, ws, pool
+    torch.cuda.empty_cache()
+    return res
+
+
+def configs_leg(zs, torch, W, dev, hp, launches: int):
+    """The fused reduce + AdamW kernel alone on the rank shards of the other
+    workloads (one launch over each whole shard, contributions resident):
+    3.3M GPT at D=4, one LLaMA-7B block at D=8, the full LLaMA-7B at D=32
+    (Student-t gradients) and the 10,000-tensor ragged unit at D=16 with fp32
+    contributions. Reports the average launch time and HBM GB/s at the
+    algorithmic 26 + D * es bytes per param."""
+    res = {}
+    for name in ("gpt3m", "llama7b_block", "llama7b_full", "ragged"):
+        w = W.get(name)
+        S = int(sum(zs.zs_unit_layout(u.numels, w.D)[3] for u in w.units))
+        es = 2 if w.reduce_dtype == "bf16" else 4
+        p = W.master_init(S, 7000 + w.index, dev)
+        m = torch.zeros(S, device=dev)
+        v = torch.zeros(S, device=dev)
+        ws = torch.empty(S, dtype=torch.int16, device=dev)
+        mask = W.step_mask(w, S, 1, 0, dev)
+        cs = [W.contribution(w, S, 1, 0, k, dev, mask) for k in range(w.D)]
+        del mask
+        zs.zs_adamw_step(p, m, v, ws, cs, dict(step=1, **hp))      # warm
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for t in range(2, 2 + launches):
+            zs.zs_adamw_step(p, m, v, ws, cs, dict(step=t, **hp))
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        bpp = 26 + w.D * es
+        res[name] = {"shard_params": S, "D": w.D, "reduce_dtype": w.reduce_dtype,
+                     "bytes_per_param": bpp, "launch_ms": ms,
+                     "params_per_s": S / (ms / 1e3), "GB_s": bpp * S / (ms / 1e3) / 1e9}
+        del p, m, v, ws, cs
+        torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the fused-kernel rates on the other workloads' shards")
+    ap.add_argument("--no-hybrid", action="store_true",
+                    help="skip the HYBRID_SHARD (4 nodes x 8 GPUs, LLaMA-7B) step leg")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the per-bucket streamed (overlapped) step leg")
     ap.add_argument("--copy-calibrate", action="store_true",
@@ -317,6 +412,12 @@ def main() -> int:
         log("pipeline leg: contributions streamed per bucket, overlapped with the step")
         out["pipeline"] = pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D,
                                        args.warmup + K + 1, hp, host_buckets=16)
+    if not args.no_hybrid:
+        log("hybrid leg: LLaMA-7B rank shard under HYBRID_SHARD, 4 x 8 contributions")
+        out["hybrid_shard"] = hybrid_leg(zs, torch, W, dev, hp, steps=3)
+    if not args.no_configs:
+        log("configs leg: the fused kernel on the other workloads' rank shards")
+        out["other_workloads"] = configs_leg(zs, torch, W, dev, hp, launches=10)
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on one block bucket (host copies)")
         sl, sz, cs, _, _ = buckets[0]

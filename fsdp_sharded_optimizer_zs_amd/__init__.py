@@ -8,12 +8,14 @@ The work runs in the HIP kernels of libzs.so; this package is its binding.
 from ._binding import (  # noqa: F401
     AdamWHP, LIB_PATH, ZS_BF16, ZS_EALIAS, ZS_EHIP, ZS_EINVAL, ZS_EUNSUPPORTED, ZS_F32,
     ZS_MAX_D, ZS_OK, ZsError, load, raw_adamw_step, zs_abi_version, zs_adamw_step,
+    zs_adamw_step_ex, zs_reduce_shard_ex,
     zs_gather_unit, zs_last_error, zs_pack_flat, zs_reduce_shard, zs_step_pipelined,
     zs_unit_layout,
 )
 
 __all__ = [
     "zs_unit_layout", "zs_pack_flat", "zs_reduce_shard", "zs_adamw_step",
+    "zs_reduce_shard_ex", "zs_adamw_step_ex",
     "zs_gather_unit", "zs_step_pipelined", "zs_last_error", "zs_abi_version", "AdamWHP", "ZsError",
     "ZS_BF16", "ZS_F32", "ZS_MAX_D", "load",
 ]

@@ -40,6 +40,10 @@ class zs_bucket(ctypes.Structure):
                 ("sources", ctypes.POINTER(ctypes.c_void_p))]
 
 
+class zs_reduce_opts(ctypes.Structure):
+    _fields_ = [("replicas", ctypes.c_int32), ("round_to_reduce_dtype", ctypes.c_int32)]
+
+
 class zs_adamw_hp(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
@@ -78,6 +82,9 @@ def load() -> ctypes.CDLL:
                 "zs_reduce_shard": (i32, [P(vp), i32, i32, i64, vp, vp]),
                 "zs_adamw_step": (i32, [vp, vp, vp, vp, i64, P(vp), i32, i32,
                                         P(zs_adamw_hp), vp]),
+                "zs_reduce_shard_ex": (i32, [P(vp), i32, P(zs_reduce_opts), i32, i64, vp, vp]),
+                "zs_adamw_step_ex": (i32, [vp, vp, vp, vp, i64, P(vp), i32, P(zs_reduce_opts),
+                                           i32, P(zs_adamw_hp), vp]),
                 "zs_gather_unit": (i32, [P(vp), i32, i64, i32, vp, vp]),
                 "zs_step_pipelined": (i32, [P(zs_bucket), i32, i32, i32, vp, vp, i64,
                                             P(zs_adamw_hp), vp, vp]),
@@ -228,6 +235,59 @@ def zs_adamw_step(p, m, v, w_out, contribs: Sequence, hp, stream=None) -> None:
                                 ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(w_out.data_ptr()),
                                 S, _ptr_array(contribs), len(contribs), code,
                                 ctypes.byref(h), _stream(p, stream)))
+
+
+def _groups(contribs: Sequence, replicas: int) -> int:
+    if replicas < 1 or len(contribs) % replicas:
+        raise ValueError("contributions must form `replicas` equal groups")
+    return len(contribs) // replicas
+
+
+def zs_reduce_shard_ex(contribs: Sequence, grad_out, replicas: int = 1,
+                       round_to_reduce_dtype: bool = False, stream=None) -> None:
+    """grad_out (fp32, S) = HYBRID_SHARD reduce of replicas groups of
+    contributions (replica-major), optionally rounding each level's output to
+    the reduce dtype."""
+    S = grad_out.numel()
+    _dev(grad_out, "grad_out")
+    if grad_out.dtype != _torch().float32:
+        raise TypeError("grad_out must be float32")
+    code = _dtype_code(contribs[0]) if contribs else ZS_F32
+    for i, c in enumerate(contribs):
+        _dev(c, f"contribs[{i}]")
+        if c.numel() != S or _dtype_code(c) != code:
+            raise ValueError("contributions must share one dtype and hold S elements")
+    D = _groups(contribs, replicas)
+    opts = zs_reduce_opts(int(replicas), 1 if round_to_reduce_dtype else 0)
+    _check(load().zs_reduce_shard_ex(_ptr_array(contribs), D, ctypes.byref(opts), code, S,
+                                     ctypes.c_void_p(grad_out.data_ptr()),
+                                     _stream(grad_out, stream)))
+
+
+def zs_adamw_step_ex(p, m, v, w_out, contribs: Sequence, hp, replicas: int = 1,
+                     round_to_reduce_dtype: bool = False, stream=None) -> None:
+    """zs_adamw_step with the reduce of zs_reduce_shard_ex."""
+    torch = _torch()
+    S = p.numel()
+    for name, t in (("p", p), ("m", m), ("v", v)):
+        _dev(t, name)
+        if t.dtype != torch.float32 or t.numel() != S:
+            raise ValueError(f"{name} must be float32 with S = {S} elements")
+    _dev(w_out, "w_out")
+    if _dtype_code(w_out) != ZS_BF16 or w_out.numel() != S:
+        raise ValueError("w_out must be bf16 bits with S elements")
+    code = _dtype_code(contribs[0]) if contribs else ZS_F32
+    for i, c in enumerate(contribs):
+        _dev(c, f"contribs[{i}]")
+        if c.numel() != S or _dtype_code(c) != code:
+            raise ValueError("contributions must share one dtype and hold S elements")
+    D = _groups(contribs, replicas)
+    opts = zs_reduce_opts(int(replicas), 1 if round_to_reduce_dtype else 0)
+    h = _hp(hp)
+    _check(load().zs_adamw_step_ex(ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(m.data_ptr()),
+                                   ctypes.c_void_p(v.data_ptr()),
+                                   ctypes.c_void_p(w_out.data_ptr()), S, _ptr_array(contribs), D,
+                                   ctypes.byref(opts), code, ctypes.byref(h), _stream(p, stream)))
 
 
 def zs_gather_unit(shards: Sequence, flat_out, stream=None) -> None:

@@ -133,7 +133,7 @@ using namespace zs;
 
 ZS_EXPORT const char* zs_last_error(void) { return g_last_error.c_str(); }
 
-ZS_EXPORT int32_t zs_abi_version(void) { return 101; }
+ZS_EXPORT int32_t zs_abi_version(void) { return 102; }
 
 ZS_EXPORT zs_status zs_unit_layout(const int64_t* numels, int32_t T, int32_t D,
                                    int64_t* offsets_out, int64_t* n_out, int64_t* n_pad_out,
@@ -210,47 +210,76 @@ ZS_EXPORT zs_status zs_pack_flat(const zs_tensor_ref* h_table, const zs_tensor_r
     return hip_status(launch_pack(d_table, T, N, es, D, sp, S, stream), "zs_pack_flat launch");
 }
 
-ZS_EXPORT zs_status zs_reduce_shard(const void* const* contribs, int32_t D, int32_t dtype,
-                                    int64_t S, float* grad_out, hipStream_t stream) {
+namespace {
+
+// Validates a reduce description: nd contributions per group, R groups.
+zs_status check_groups(const char* who, int32_t nd, const zs_reduce_opts* opts, int* R,
+                       bool* rnd) {
+    *R = 1;
+    *rnd = false;
+    if (opts != nullptr) {
+        if (opts->replicas < 1)
+            return fail(ZS_EINVAL, "%s: replicas = %d < 1", who, opts->replicas);
+        if (opts->round_to_reduce_dtype != 0 && opts->round_to_reduce_dtype != 1)
+            return fail(ZS_EINVAL, "%s: round_to_reduce_dtype must be 0 or 1", who);
+        *R = opts->replicas;
+        *rnd = opts->round_to_reduce_dtype == 1;
+    }
+    if (nd < 1 || nd > ZS_MAX_D)
+        return fail(ZS_EINVAL, "%s: D = %d outside 1..%d", who, nd, ZS_MAX_D);
+    if (int64_t(*R) * nd > ZS_MAX_D)
+        return fail(ZS_EINVAL, "%s: replicas * D = %lld exceeds %d contributions", who,
+                    (long long)(int64_t(*R) * nd), ZS_MAX_D);
+    return ZS_OK;
+}
+
+zs_status reduce_common(const char* who, const void* const* contribs, int32_t nd,
+                        const zs_reduce_opts* opts, int32_t dtype, int64_t S, float* grad_out,
+                        hipStream_t stream) {
     const int es = elem_size(dtype);
-    if (es == 0) return fail(ZS_EUNSUPPORTED, "zs_reduce_shard: unknown dtype %d", dtype);
-    if (D < 1 || D > ZS_MAX_D)
-        return fail(ZS_EINVAL, "zs_reduce_shard: D = %d outside 1..%d", D, ZS_MAX_D);
-    if (!size_ok(S, 4)) return fail(ZS_EINVAL, "zs_reduce_shard: S = %lld out of range", (long long)S);
+    if (es == 0) return fail(ZS_EUNSUPPORTED, "%s: unknown dtype %d", who, dtype);
+    int R;
+    bool rnd;
+    zs_status st = check_groups(who, nd, opts, &R, &rnd);
+    if (st != ZS_OK) return st;
+    if (!size_ok(S, 4)) return fail(ZS_EINVAL, "%s: S = %lld out of range", who, (long long)S);
     if (S == 0) return ok();
-    if (grad_out == nullptr) return fail(ZS_EINVAL, "zs_reduce_shard: grad_out is NULL");
-    if (!aligned(grad_out, 4)) return fail(ZS_EINVAL, "zs_reduce_shard: grad_out not 4-byte aligned");
+    if (grad_out == nullptr) return fail(ZS_EINVAL, "%s: grad_out is NULL", who);
+    if (!aligned(grad_out, 4)) return fail(ZS_EINVAL, "%s: grad_out not 4-byte aligned", who);
+    const int n = R * nd;
     PtrPack cp;
-    zs_status st = take_ptrs(contribs, D, es, "zs_reduce_shard: contribs", &cp);
+    st = take_ptrs(contribs, n, es, (std::string(who) + ": contribs").c_str(), &cp);
     if (st != ZS_OK) return st;
     const Range out = range_of(grad_out, S, 4);
     bool al = aligned(grad_out, 16);
-    for (int k = 0; k < D; ++k) {
+    for (int k = 0; k < n; ++k) {
         if (overlap(out, range_of(cp.p[k], S, es)))
-            return fail(ZS_EALIAS, "zs_reduce_shard: grad_out overlaps contribution %d", k);
+            return fail(ZS_EALIAS, "%s: grad_out overlaps contribution %d", who, k);
         al = al && aligned(cp.p[k], 16);
     }
-    const float inv_n = float(1.0 / double(D));
-    return hip_status(launch_reduce(cp, D, dtype, S, inv_n, grad_out, al, stream),
-                      "zs_reduce_shard launch");
+    const float inv_n = float(1.0 / double(n));
+    return hip_status(launch_reduce(cp, nd, R, rnd, dtype, S, inv_n, grad_out, al, stream), who);
 }
 
-ZS_EXPORT zs_status zs_adamw_step(float* p, float* m, float* v, uint16_t* w_out, int64_t S,
-                                  const void* const* contribs, int32_t n_contrib, int32_t dtype,
-                                  const zs_adamw_hp* hp, hipStream_t stream) {
+zs_status adamw_common(const char* who, float* p, float* m, float* v, uint16_t* w_out, int64_t S,
+                       const void* const* contribs, int32_t nd, const zs_reduce_opts* opts,
+                       int32_t dtype, const zs_adamw_hp* hp, hipStream_t stream) {
     const int es = elem_size(dtype);
-    if (es == 0) return fail(ZS_EUNSUPPORTED, "zs_adamw_step: unknown dtype %d", dtype);
-    if (n_contrib < 1 || n_contrib > ZS_MAX_D)
-        return fail(ZS_EINVAL, "zs_adamw_step: n_contrib = %d outside 1..%d", n_contrib, ZS_MAX_D);
-    if (!size_ok(S, 4)) return fail(ZS_EINVAL, "zs_adamw_step: S = %lld out of range", (long long)S);
-    zs_status st = check_hp(hp, "zs_adamw_step");
+    if (es == 0) return fail(ZS_EUNSUPPORTED, "%s: unknown dtype %d", who, dtype);
+    int R;
+    bool rnd;
+    zs_status st = check_groups(who, nd, opts, &R, &rnd);
+    if (st != ZS_OK) return st;
+    if (!size_ok(S, 4)) return fail(ZS_EINVAL, "%s: S = %lld out of range", who, (long long)S);
+    st = check_hp(hp, who);
     if (st != ZS_OK) return st;
     if (S == 0) return ok();
-    if (!p || !m || !v || !w_out) return fail(ZS_EINVAL, "zs_adamw_step: p, m, v or w_out is NULL");
+    if (!p || !m || !v || !w_out) return fail(ZS_EINVAL, "%s: p, m, v or w_out is NULL", who);
     if (!aligned(p, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(w_out, 2))
-        return fail(ZS_EINVAL, "zs_adamw_step: p, m, v or w_out misaligned for its element type");
+        return fail(ZS_EINVAL, "%s: p, m, v or w_out misaligned for its element type", who);
+    const int n = R * nd;
     PtrPack cp;
-    st = take_ptrs(contribs, n_contrib, es, "zs_adamw_step: contribs", &cp);
+    st = take_ptrs(contribs, n, es, (std::string(who) + ": contribs").c_str(), &cp);
     if (st != ZS_OK) return st;
     const Range rs[4] = {range_of(p, S, 4), range_of(m, S, 4), range_of(v, S, 4),
                          range_of(w_out, S, 2)};
@@ -258,19 +287,45 @@ ZS_EXPORT zs_status zs_adamw_step(float* p, float* m, float* v, uint16_t* w_out,
     for (int a = 0; a < 4; ++a)
         for (int b = a + 1; b < 4; ++b)
             if (overlap(rs[a], rs[b]))
-                return fail(ZS_EALIAS, "zs_adamw_step: %s overlaps %s", names[a], names[b]);
+                return fail(ZS_EALIAS, "%s: %s overlaps %s", who, names[a], names[b]);
     bool al = aligned(p, 16) && aligned(m, 16) && aligned(v, 16) && aligned(w_out, 16);
-    for (int k = 0; k < n_contrib; ++k) {
+    for (int k = 0; k < n; ++k) {
         const Range c = range_of(cp.p[k], S, es);
         for (int a = 0; a < 4; ++a)
             if (overlap(c, rs[a]))
-                return fail(ZS_EALIAS, "zs_adamw_step: contribution %d overlaps %s", k, names[a]);
+                return fail(ZS_EALIAS, "%s: contribution %d overlaps %s", who, k, names[a]);
         al = al && aligned(cp.p[k], 16);
     }
+    const AdamConsts k = adam_consts(*hp, n);
+    return hip_status(launch_adamw(p, m, v, w_out, S, cp, nd, R, rnd, dtype, k, al, stream), who);
+}
 
-    const AdamConsts k = adam_consts(*hp, n_contrib);
-    return hip_status(launch_adamw(p, m, v, w_out, S, cp, n_contrib, dtype, k, al, stream),
-                      "zs_adamw_step launch");
+}  // namespace
+
+ZS_EXPORT zs_status zs_reduce_shard(const void* const* contribs, int32_t D, int32_t dtype,
+                                    int64_t S, float* grad_out, hipStream_t stream) {
+    return reduce_common("zs_reduce_shard", contribs, D, nullptr, dtype, S, grad_out, stream);
+}
+
+ZS_EXPORT zs_status zs_reduce_shard_ex(const void* const* contribs, int32_t D,
+                                       const zs_reduce_opts* opts, int32_t dtype, int64_t S,
+                                       float* grad_out, hipStream_t stream) {
+    return reduce_common("zs_reduce_shard_ex", contribs, D, opts, dtype, S, grad_out, stream);
+}
+
+ZS_EXPORT zs_status zs_adamw_step(float* p, float* m, float* v, uint16_t* w_out, int64_t S,
+                                  const void* const* contribs, int32_t n_contrib, int32_t dtype,
+                                  const zs_adamw_hp* hp, hipStream_t stream) {
+    return adamw_common("zs_adamw_step", p, m, v, w_out, S, contribs, n_contrib, nullptr, dtype,
+                        hp, stream);
+}
+
+ZS_EXPORT zs_status zs_adamw_step_ex(float* p, float* m, float* v, uint16_t* w_out, int64_t S,
+                                     const void* const* contribs, int32_t D,
+                                     const zs_reduce_opts* opts, int32_t dtype,
+                                     const zs_adamw_hp* hp, hipStream_t stream) {
+    return adamw_common("zs_adamw_step_ex", p, m, v, w_out, S, contribs, D, opts, dtype, hp,
+                        stream);
 }
 
 ZS_EXPORT zs_status zs_gather_unit(const void* const* shards, int32_t D, int64_t S,

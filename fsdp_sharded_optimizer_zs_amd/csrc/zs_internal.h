@@ -49,11 +49,13 @@ struct DeviceInfo {
 };
 const DeviceInfo& device_info();
 
-// Kernel launchers (enqueue only; return the launch status).
+// Kernel launchers (enqueue only; return the launch status). The reduce of
+// the step folds R groups of nd contributions (replica-major; R = 1 is the
+// flat fold), rounding each level to the reduce dtype when rnd is set.
 hipError_t launch_adamw(float* p, float* m, float* v, uint16_t* w, int64_t S,
-                        const PtrPack& contribs, int n, int dtype,
+                        const PtrPack& contribs, int nd, int R, bool rnd, int dtype,
                         const AdamConsts& k, bool aligned, hipStream_t stream);
-hipError_t launch_reduce(const PtrPack& contribs, int n, int dtype, int64_t S,
+hipError_t launch_reduce(const PtrPack& contribs, int nd, int R, bool rnd, int dtype, int64_t S,
                          float inv_n, float* out, bool aligned, hipStream_t stream);
 hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es,
                        int D, const PtrPack& shards, int64_t S, hipStream_t stream);

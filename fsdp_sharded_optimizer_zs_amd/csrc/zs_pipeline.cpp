@@ -155,7 +155,8 @@ ZS_EXPORT zs_status zs_step_pipelined(const zs_bucket* buckets, int32_t n_bucket
         // compute: wait for this bucket's contributions, step, release the slot
         if ((e = hipStreamWaitEvent(compute, ev.arrived[s], 0)) != hipSuccess)
             return hip_status(e, "zs_step_pipelined: compute wait");
-        e = launch_adamw(k.p, k.m, k.v, k.w_out, k.S, staged, n_contrib, dtype, kc, al, compute);
+        e = launch_adamw(k.p, k.m, k.v, k.w_out, k.S, staged, n_contrib, 1, false, dtype, kc, al,
+                         compute);
         if (e != hipSuccess) return hip_status(e, "zs_step_pipelined: step launch");
         if ((e = hipEventRecord(ev.consumed[s], compute)) != hipSuccess)
             return hip_status(e, "zs_step_pipelined: event record");

@@ -108,38 +108,114 @@ __device__ __forceinline__ float load1(const void* base, int64_t i) {
     }
 }
 
-// g = ((c_0 + c_1) + ... + c_{n-1}) * inv_n for 8 elements, in rank order.
+// Fold of the n contributions c.p[base .. base+n) for 8 elements, left to
+// right from the first, into s (fp32, one rounding per add). Loads are
+// issued in batches of up to 8 contributions ahead of their adds; the add
+// order is the plain left fold whatever the batching. (A fully unrolled
+// fold of 16 or 32 contributions lets the compiler interleave loads and
+// adds, which measured 25% slower at 32.)
+constexpr int kBatch = 8;
+
+template <int DT, int NB>
+__device__ __forceinline__ void add_batch(const PtrPack& c, int first, int64_t i,
+                                          float (&s)[kVec]) {
+    float x[NB][kVec];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) load8<DT>(c.p[first + q], i, x[q]);
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) s[e] = s[e] + x[q][e];
+}
+
 template <int DT, int NC>
-__device__ __forceinline__ void reduce8(const PtrPack& c, int n, float inv_n, int64_t i,
-                                        float (&g)[kVec]) {
-    load8<DT>(c.p[0], i, g);
-    if constexpr (NC > 0) {
-#pragma unroll
-        for (int q = 1; q < NC; ++q) {
-            float x[kVec];
-            load8<DT>(c.p[q], i, x);
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) g[e] = g[e] + x[e];
-        }
+__device__ __forceinline__ void fold8(const PtrPack& c, int base, int n, int64_t i,
+                                      float (&s)[kVec]) {
+    if constexpr (NC > 0 && NC <= kBatch) {
+        load8<DT>(c.p[base], i, s);
+        if constexpr (NC > 1) add_batch<DT, NC - 1>(c, base + 1, i, s);
     } else {
-#pragma unroll 4
-        for (int q = 1; q < n; ++q) {
-            float x[kVec];
-            load8<DT>(c.p[q], i, x);
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) g[e] = g[e] + x[e];
+        const int len = NC > 0 ? NC : n;
+        // first batch: c_0 then up to 7 more
+        const int head = len < kBatch ? len : kBatch;
+        load8<DT>(c.p[base], i, s);
+        int q = 1;
+        if (head == kBatch) {
+            add_batch<DT, kBatch - 1>(c, base + 1, i, s);
+            q = kBatch;
         }
+#pragma unroll 1
+        for (; q + kBatch <= len; q += kBatch) add_batch<DT, kBatch>(c, base + q, i, s);
+#pragma unroll 1
+        for (; q < len; ++q) add_batch<DT, 1>(c, base + q, i, s);
     }
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) g[e] = g[e] * inv_n;
 }
 
 template <int DT>
-__device__ __forceinline__ float reduce1(const PtrPack& c, int n, float inv_n, int64_t i) {
-    float s = load1<DT>(c.p[0], i);
-    for (int q = 1; q < n; ++q) s = s + load1<DT>(c.p[q], i);
-    return s * inv_n;
+__device__ __forceinline__ float fold1(const PtrPack& c, int base, int n, int64_t i) {
+    float s = load1<DT>(c.p[base], i);
+    for (int q = 1; q < n; ++q) s = s + load1<DT>(c.p[base + q], i);
+    return s;
 }
+
+// The value an fp32 partial sum takes once held in the reduce dtype.
+template <int DT>
+__device__ __forceinline__ float to_reduce_dtype(float x) {
+    if constexpr (DT == ZS_BF16) return __uint_as_float(f32_to_bf16(x) << 16);
+    return x;
+}
+
+// Flat reduce: g = ((c_0 + c_1) + ... + c_{n-1}) * inv_n, in rank order.
+// NC > 0 fixes n at compile time so every load is issued before the adds.
+template <int DT, int NC>
+struct FlatSum {
+    int n;
+    float inv_n;
+    __device__ __forceinline__ void vec(const PtrPack& c, int64_t i, float (&g)[kVec]) const {
+        fold8<DT, NC>(c, 0, n, i, g);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) g[e] = g[e] * inv_n;
+    }
+    __device__ __forceinline__ float one(const PtrPack& c, int64_t i) const {
+        return fold1<DT>(c, 0, n, i) * inv_n;
+    }
+};
+
+// HYBRID_SHARD reduce: R replica groups of nd contributions each, replica-
+// major (c.p[j*nd + k]). Group j folds to s_j; with rnd, s_j is rounded to
+// the reduce dtype (a collective's output held in it); the s_j fold left in
+// group order to t, rounded again with rnd; g = t * inv_n, inv_n = 1/(R*nd).
+template <int DT, int NC>
+struct HybridSum {
+    int nd;
+    int R;
+    int rnd;
+    float inv_n;
+    __device__ __forceinline__ void vec(const PtrPack& c, int64_t i, float (&g)[kVec]) const {
+        fold8<DT, NC>(c, 0, nd, i, g);
+        if (rnd) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) g[e] = to_reduce_dtype<DT>(g[e]);
+        }
+        for (int j = 1; j < R; ++j) {
+            float s[kVec];
+            fold8<DT, NC>(c, j * nd, nd, i, s);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) g[e] = g[e] + (rnd ? to_reduce_dtype<DT>(s[e]) : s[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) g[e] = (rnd ? to_reduce_dtype<DT>(g[e]) : g[e]) * inv_n;
+    }
+    __device__ __forceinline__ float one(const PtrPack& c, int64_t i) const {
+        float t = fold1<DT>(c, 0, nd, i);
+        if (rnd) t = to_reduce_dtype<DT>(t);
+        for (int j = 1; j < R; ++j) {
+            const float s = fold1<DT>(c, j * nd, nd, i);
+            t = t + (rnd ? to_reduce_dtype<DT>(s) : s);
+        }
+        return (rnd ? to_reduce_dtype<DT>(t) : t) * inv_n;
+    }
+};
 
 // One AdamW element, in the fixed order, every operation rounded on its own.
 __device__ __forceinline__ void adamw1(float& p, float& m, float& v, float g,
@@ -157,10 +233,10 @@ __device__ __forceinline__ void adamw1(float& p, float& m, float& v, float g,
 
 // Fused reduce + AdamW over 8-element vectors; 16-byte aligned buffers.
 // The last block also handles the S % 8 tail elements one per lane.
-template <int DT, int NC>
+template <int DT, class Sum>
 __global__ __launch_bounds__(kThreads) void adamw_vec_kernel(
     float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
-    uint16_t* __restrict__ w, int64_t S, PtrPack c, int n, AdamConsts k) {
+    uint16_t* __restrict__ w, int64_t S, PtrPack c, Sum sum, AdamConsts k) {
     const int64_t nvec = S / kVec;
     const int64_t stride = int64_t(gridDim.x) * kThreads;
     f32x4* p4 = reinterpret_cast<f32x4*>(p);
@@ -169,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void adamw_vec_kernel(
     u32x4* w4 = reinterpret_cast<u32x4*>(w);
     for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride) {
         float g[kVec];
-        reduce8<DT, NC>(c, n, k.inv_n, i, g);
+        sum.vec(c, i, g);
         const f32x4 pa = p4[2 * i], pb = p4[2 * i + 1];
         const f32x4 ma = m4[2 * i], mb = m4[2 * i + 1];
         const f32x4 va = v4[2 * i], vb = v4[2 * i + 1];
@@ -195,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void adamw_vec_kernel(
     }
     const int64_t t = nvec * kVec + threadIdx.x;
     if (blockIdx.x == gridDim.x - 1 && t < S) {
-        const float g = reduce1<DT>(c, n, k.inv_n, t);
+        const float g = sum.one(c, t);
         float pp = p[t], mm = m[t], vv = v[t];
         adamw1(pp, mm, vv, g, k);
         p[t] = pp;
@@ -206,13 +282,13 @@ __global__ __launch_bounds__(kThreads) void adamw_vec_kernel(
 }
 
 // Element-at-a-time variant for buffers that are not 16-byte aligned.
-template <int DT>
+template <int DT, class Sum>
 __global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(
     float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
-    uint16_t* __restrict__ w, int64_t S, PtrPack c, int n, AdamConsts k) {
+    uint16_t* __restrict__ w, int64_t S, PtrPack c, Sum sum, AdamConsts k) {
     const int64_t stride = int64_t(gridDim.x) * kThreads;
     for (int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x; t < S; t += stride) {
-        const float g = reduce1<DT>(c, n, k.inv_n, t);
+        const float g = sum.one(c, t);
         float pp = p[t], mm = m[t], vv = v[t];
         adamw1(pp, mm, vv, g, k);
         p[t] = pp;
@@ -223,28 +299,28 @@ __global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(
 }
 
 // Unfused reduce: g written to HBM (fp32).
-template <int DT, int NC>
-__global__ __launch_bounds__(kThreads) void reduce_vec_kernel(
-    float* __restrict__ out, int64_t S, PtrPack c, int n, float inv_n) {
+template <int DT, class Sum>
+__global__ __launch_bounds__(kThreads) void reduce_vec_kernel(float* __restrict__ out, int64_t S,
+                                                              PtrPack c, Sum sum) {
     const int64_t nvec = S / kVec;
     const int64_t stride = int64_t(gridDim.x) * kThreads;
     f32x4* o4 = reinterpret_cast<f32x4*>(out);
     for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride) {
         float g[kVec];
-        reduce8<DT, NC>(c, n, inv_n, i, g);
+        sum.vec(c, i, g);
         st_once(f32x4{g[0], g[1], g[2], g[3]}, o4 + 2 * i);
         st_once(f32x4{g[4], g[5], g[6], g[7]}, o4 + 2 * i + 1);
     }
     const int64_t t = nvec * kVec + threadIdx.x;
-    if (blockIdx.x == gridDim.x - 1 && t < S) out[t] = reduce1<DT>(c, n, inv_n, t);
+    if (blockIdx.x == gridDim.x - 1 && t < S) out[t] = sum.one(c, t);
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void reduce_scalar_kernel(
-    float* __restrict__ out, int64_t S, PtrPack c, int n, float inv_n) {
+template <int DT, class Sum>
+__global__ __launch_bounds__(kThreads) void reduce_scalar_kernel(float* __restrict__ out,
+                                                                 int64_t S, PtrPack c, Sum sum) {
     const int64_t stride = int64_t(gridDim.x) * kThreads;
     for (int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x; t < S; t += stride)
-        out[t] = reduce1<DT>(c, n, inv_n, t);
+        out[t] = sum.one(c, t);
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -256,77 +332,84 @@ int grid_for(int64_t work_items) {
     return blocks < 1 ? 1 : int(blocks);
 }
 
-template <int DT, int NC>
-hipError_t adamw_vec_launch(float* p, float* m, float* v, uint16_t* w, int64_t S,
-                            const PtrPack& c, int n, const AdamConsts& k,
-                            hipStream_t stream) {
-    hipLaunchKernelGGL((adamw_vec_kernel<DT, NC>), dim3(grid_for(S / kVec)), dim3(kThreads),
-                       0, stream, p, m, v, w, S, c, n, k);
+// What one launch computes: the AdamW step (out == nullptr) or the reduce
+// alone into out.
+struct Job {
+    float* p;
+    float* m;
+    float* v;
+    uint16_t* w;
+    float* out;
+    int64_t S;
+    AdamConsts k;
+    bool aligned;
+};
+
+template <int DT, class Sum>
+hipError_t launch_job(const Job& j, const PtrPack& c, const Sum& sum, hipStream_t stream) {
+    if (j.out == nullptr) {
+        if (j.aligned)
+            hipLaunchKernelGGL((adamw_vec_kernel<DT, Sum>), dim3(grid_for(j.S / kVec)),
+                               dim3(kThreads), 0, stream, j.p, j.m, j.v, j.w, j.S, c, sum, j.k);
+        else
+            hipLaunchKernelGGL((adamw_scalar_kernel<DT, Sum>), dim3(grid_for(j.S)), dim3(kThreads),
+                               0, stream, j.p, j.m, j.v, j.w, j.S, c, sum, j.k);
+    } else {
+        if (j.aligned)
+            hipLaunchKernelGGL((reduce_vec_kernel<DT, Sum>), dim3(grid_for(j.S / kVec)),
+                               dim3(kThreads), 0, stream, j.out, j.S, c, sum);
+        else
+            hipLaunchKernelGGL((reduce_scalar_kernel<DT, Sum>), dim3(grid_for(j.S)),
+                               dim3(kThreads), 0, stream, j.out, j.S, c, sum);
+    }
     return hipGetLastError();
 }
 
-template <int DT>
-hipError_t adamw_dispatch(float* p, float* m, float* v, uint16_t* w, int64_t S,
-                          const PtrPack& c, int n, const AdamConsts& k, bool aligned,
-                          hipStream_t stream) {
-    if (!aligned) {
-        hipLaunchKernelGGL((adamw_scalar_kernel<DT>), dim3(grid_for(S)), dim3(kThreads), 0,
-                           stream, p, m, v, w, S, c, n, k);
-        return hipGetLastError();
-    }
-    switch (n) {
-        case 1: return adamw_vec_launch<DT, 1>(p, m, v, w, S, c, n, k, stream);
-        case 2: return adamw_vec_launch<DT, 2>(p, m, v, w, S, c, n, k, stream);
-        case 4: return adamw_vec_launch<DT, 4>(p, m, v, w, S, c, n, k, stream);
-        case 8: return adamw_vec_launch<DT, 8>(p, m, v, w, S, c, n, k, stream);
-        case 16: return adamw_vec_launch<DT, 16>(p, m, v, w, S, c, n, k, stream);
-        case 32: return adamw_vec_launch<DT, 32>(p, m, v, w, S, c, n, k, stream);
-        default: return adamw_vec_launch<DT, 0>(p, m, v, w, S, c, n, k, stream);
+// Compile-time fold length for the common group sizes (all loads of a group
+// in flight before its adds); a runtime loop for the others. The scalar
+// kernels take the runtime form only.
+template <int DT, template <int, int> class SumT, class Make>
+hipError_t dispatch_nc(const Job& j, const PtrPack& c, int nc, Make make, hipStream_t stream) {
+    if (!j.aligned) return launch_job<DT>(j, c, make(SumT<DT, 0>{}), stream);
+    switch (nc) {
+        case 1: return launch_job<DT>(j, c, make(SumT<DT, 1>{}), stream);
+        case 2: return launch_job<DT>(j, c, make(SumT<DT, 2>{}), stream);
+        case 4: return launch_job<DT>(j, c, make(SumT<DT, 4>{}), stream);
+        case 8: return launch_job<DT>(j, c, make(SumT<DT, 8>{}), stream);
+        case 16: return launch_job<DT>(j, c, make(SumT<DT, 16>{}), stream);
+        case 32: return launch_job<DT>(j, c, make(SumT<DT, 32>{}), stream);
+        default: return launch_job<DT>(j, c, make(SumT<DT, 0>{}), stream);
     }
 }
 
-template <int DT, int NC>
-hipError_t reduce_vec_launch(const PtrPack& c, int n, int64_t S, float inv_n, float* out,
-                             hipStream_t stream) {
-    hipLaunchKernelGGL((reduce_vec_kernel<DT, NC>), dim3(grid_for(S / kVec)), dim3(kThreads),
-                       0, stream, out, S, c, n, inv_n);
-    return hipGetLastError();
-}
-
 template <int DT>
-hipError_t reduce_dispatch(const PtrPack& c, int n, int64_t S, float inv_n, float* out,
-                           bool aligned, hipStream_t stream) {
-    if (!aligned) {
-        hipLaunchKernelGGL((reduce_scalar_kernel<DT>), dim3(grid_for(S)), dim3(kThreads), 0,
-                           stream, out, S, c, n, inv_n);
-        return hipGetLastError();
-    }
-    switch (n) {
-        case 1: return reduce_vec_launch<DT, 1>(c, n, S, inv_n, out, stream);
-        case 2: return reduce_vec_launch<DT, 2>(c, n, S, inv_n, out, stream);
-        case 4: return reduce_vec_launch<DT, 4>(c, n, S, inv_n, out, stream);
-        case 8: return reduce_vec_launch<DT, 8>(c, n, S, inv_n, out, stream);
-        case 16: return reduce_vec_launch<DT, 16>(c, n, S, inv_n, out, stream);
-        case 32: return reduce_vec_launch<DT, 32>(c, n, S, inv_n, out, stream);
-        default: return reduce_vec_launch<DT, 0>(c, n, S, inv_n, out, stream);
-    }
+hipError_t dispatch(const Job& j, const PtrPack& c, int nd, int R, bool rnd, hipStream_t stream) {
+    const float inv_n = j.k.inv_n;
+    if (R == 1 && !rnd)
+        return dispatch_nc<DT, FlatSum>(j, c, nd, [&](auto s) { s.n = nd; s.inv_n = inv_n; return s; },
+                                        stream);
+    return dispatch_nc<DT, HybridSum>(
+        j, c, nd, [&](auto s) { s.nd = nd; s.R = R; s.rnd = rnd ? 1 : 0; s.inv_n = inv_n; return s; },
+        stream);
 }
 
 }  // namespace
 
 hipError_t launch_adamw(float* p, float* m, float* v, uint16_t* w, int64_t S,
-                        const PtrPack& contribs, int n, int dtype, const AdamConsts& k,
-                        bool aligned, hipStream_t stream) {
-    if (dtype == ZS_BF16)
-        return adamw_dispatch<ZS_BF16>(p, m, v, w, S, contribs, n, k, aligned, stream);
-    return adamw_dispatch<ZS_F32>(p, m, v, w, S, contribs, n, k, aligned, stream);
+                        const PtrPack& contribs, int nd, int R, bool rnd, int dtype,
+                        const AdamConsts& k, bool aligned, hipStream_t stream) {
+    const Job j{p, m, v, w, nullptr, S, k, aligned};
+    if (dtype == ZS_BF16) return dispatch<ZS_BF16>(j, contribs, nd, R, rnd, stream);
+    return dispatch<ZS_F32>(j, contribs, nd, R, rnd, stream);
 }
 
-hipError_t launch_reduce(const PtrPack& contribs, int n, int dtype, int64_t S, float inv_n,
-                         float* out, bool aligned, hipStream_t stream) {
-    if (dtype == ZS_BF16)
-        return reduce_dispatch<ZS_BF16>(contribs, n, S, inv_n, out, aligned, stream);
-    return reduce_dispatch<ZS_F32>(contribs, n, S, inv_n, out, aligned, stream);
+hipError_t launch_reduce(const PtrPack& contribs, int nd, int R, bool rnd, int dtype, int64_t S,
+                         float inv_n, float* out, bool aligned, hipStream_t stream) {
+    AdamConsts k{};
+    k.inv_n = inv_n;
+    const Job j{nullptr, nullptr, nullptr, nullptr, out, S, k, aligned};
+    if (dtype == ZS_BF16) return dispatch<ZS_BF16>(j, contribs, nd, R, rnd, stream);
+    return dispatch<ZS_F32>(j, contribs, nd, R, rnd, stream);
 }
 
 }  // namespace zs

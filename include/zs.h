@@ -8,6 +8,8 @@
  *   zs_pack_flat     pack a unit's tensors into D contiguous shards
  *   zs_reduce_shard  reduce-scatter arithmetic for one shard
  *   zs_adamw_step    fused reduce + mixed-precision AdamW on one shard
+ *   zs_reduce_shard_ex, zs_adamw_step_ex  the same under HYBRID_SHARD's
+ *                    two-level reduce and/or reduce-dtype rounding
  *   zs_gather_unit   all-gather's local rebuild of a unit from its shards
  *   zs_step_pipelined  the step over a sequence of buckets, each bucket's
  *                    contribution transfer overlapped with the previous step
@@ -186,6 +188,55 @@ zs_status zs_reduce_shard(const void* const* contribs, int32_t D, int32_t dtype,
 zs_status zs_adamw_step(float* p, float* m, float* v, uint16_t* w_out, int64_t S,
                         const void* const* contribs, int32_t n_contrib, int32_t dtype,
                         const zs_adamw_hp* hp, hipStream_t stream);
+
+/* How the contributions of one shard are reduced (zs_reduce_shard_ex,
+ * zs_adamw_step_ex). replicas = 1 and round_to_reduce_dtype = 0 is the flat
+ * reduce of zs_reduce_shard / zs_adamw_step. */
+typedef struct {
+    int32_t replicas;               /* R >= 1 replica groups (HYBRID_SHARD nodes) */
+    int32_t round_to_reduce_dtype;  /* 0 or 1: each collective's output is held
+                                       in the reduce dtype                        */
+} zs_reduce_opts;
+
+/*
+ * zs_reduce_shard_ex -- reduce-scatter arithmetic under HYBRID_SHARD and/or
+ * with the collectives' outputs rounded to the reduce dtype.
+ *
+ * [GPT8] "Sharding Strategies" and "HYBRID_SHARD: The Multi-Node Strategy":
+ * parameters are fully sharded over the D GPUs of a node and replicated
+ * over R nodes; each node reduce-scatters over its local ranks, then the
+ * nodes all-reduce their shards. [RP] section 2 (reduce_dtype bf16) and
+ * [GPT8] "Mixed Precision" (reduce_dtype fp32) give the dtype the
+ * collectives communicate in. For i < S, with contributions replica-major
+ * (contribs[j*D + k] = local rank k of node j):
+ *   s_j = ((c_{j,0} + c_{j,1}) + ...) + c_{j,D-1}      fp32, per node j
+ *   s_j = round_to_reduce_dtype(s_j)                   if opts->round...
+ *   t   = ((s_0 + s_1) + ...) + s_{R-1}                fp32
+ *   t   = round_to_reduce_dtype(t)                     if opts->round...
+ *   grad_out[i] = t * float(1 / (R * D))
+ * where round_to_reduce_dtype is bf16 round-to-nearest-even widened back
+ * (exact identity for fp32). opts == NULL means R = 1, no rounding.
+ *
+ *   contribs  host array of R * D device pointers (R * D <= ZS_MAX_D), each
+ *             to S elements of dtype
+ *   D         contributions per node, >= 1
+ *   opts      host pointer or NULL
+ * Other arguments and errors as zs_reduce_shard; ZS_EINVAL also for
+ * replicas < 1, round_to_reduce_dtype not 0/1 or R * D > ZS_MAX_D.
+ */
+zs_status zs_reduce_shard_ex(const void* const* contribs, int32_t D, const zs_reduce_opts* opts,
+                             int32_t dtype, int64_t S, float* grad_out, hipStream_t stream);
+
+/*
+ * zs_adamw_step_ex -- zs_adamw_step with the reduce of zs_reduce_shard_ex:
+ * the gradient is the grad_out value of zs_reduce_shard_ex for these
+ * contributions and opts (never stored), then the AdamW update of
+ * zs_adamw_step, whose constants use n_contrib = R * D.
+ * Arguments and errors as zs_adamw_step and zs_reduce_shard_ex.
+ */
+zs_status zs_adamw_step_ex(float* p, float* m, float* v, uint16_t* w_out, int64_t S,
+                           const void* const* contribs, int32_t D, const zs_reduce_opts* opts,
+                           int32_t dtype, const zs_adamw_hp* hp, hipStream_t stream);
 
 /*
  * zs_gather_unit -- the local data movement of all-gather.

@@ -35,7 +35,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("zs_unit_layout", "zs_pack_flat", "zs_reduce_shard", "zs_adamw_step",
-              "zs_gather_unit", "zs_step_pipelined", "zs_last_error", "zs_abi_version"):
+              "zs_gather_unit", "zs_step_pipelined", "zs_reduce_shard_ex", "zs_adamw_step_ex",
+              "zs_last_error", "zs_abi_version"):
         assert n in names
 
 
@@ -231,3 +232,37 @@ def test_pipelined_argument_errors(lib):
     arr[0].p = A
     arr[0].S = -5
     assert run() == zs.ZS_EINVAL
+
+
+def test_hybrid_argument_errors(lib):
+    _no_gpu()
+    S = 512
+    p, m, v, w = A, A + 0x10000, A + 0x20000, A + 0x30000
+    cs = [A + 0x100000 + 0x1000 * k for k in range(64)]
+    arr = (ctypes.c_void_p * 64)(*cs)
+
+    def step(D, R, rnd, dtype=zs.ZS_BF16, hp=None):
+        o = B.zs_reduce_opts(R, rnd)
+        h = hp or _hp()
+        return lib.zs_adamw_step_ex(p, m, v, w, S, arr, D, ctypes.byref(o), dtype, ctypes.byref(h), None)
+
+    def red(D, R, rnd, out=A + 0x40000):
+        o = B.zs_reduce_opts(R, rnd)
+        return lib.zs_reduce_shard_ex(arr, D, ctypes.byref(o), zs.ZS_BF16, S, out, None)
+
+    assert step(8, 0, 0) == zs.ZS_EINVAL and "replicas" in zs.zs_last_error()
+    assert step(8, 1, 2) == zs.ZS_EINVAL and "round_to_reduce_dtype" in zs.zs_last_error()
+    assert step(8, 9, 0) == zs.ZS_EINVAL and "exceeds" in zs.zs_last_error()
+    assert step(0, 1, 0) == zs.ZS_EINVAL
+    assert step(8, 2, 1, dtype=3) == zs.ZS_EUNSUPPORTED
+    assert step(8, 2, 1, hp=_hp(step=0)) == zs.ZS_EINVAL
+    arr[17] = p + 64                       # contribution 17 (node 2) over p
+    assert step(8, 4, 1) == zs.ZS_EALIAS
+    arr[17] = cs[17]
+    arr[9] = 0
+    assert step(8, 2, 0) == zs.ZS_EINVAL and "contribs[9]" in zs.zs_last_error()
+    arr[9] = cs[9]
+    assert red(8, 0, 0) == zs.ZS_EINVAL
+    assert red(4, 2, 1, out=None) == zs.ZS_EINVAL
+    assert red(4, 2, 1, out=cs[5] + 8) == zs.ZS_EALIAS
+    assert lib.zs_reduce_shard_ex(arr, 8, None, zs.ZS_BF16, 0, None, None) == zs.ZS_OK

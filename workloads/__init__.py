@@ -19,6 +19,9 @@ Workloads (shapes from the pages; sizes are exact element counts):
 * ``llama70b``   -- the 70B shape of the multi-node section of the Part 8 page
   (80 blocks, d = 8192, GQA k/v 1024 wide, FFN 28672, vocab 32000), rank 0's
   shard at D = 8, one bucket per unit.
+* ``llama7b_hybrid`` -- the full LLaMA-7B under HYBRID_SHARD as in the Part 8
+  page's multi-node profile (4 nodes x 8 GPUs): rank 0's shard at D = 8 with
+  4 replica groups of 8 bf16 contributions, collectives held in bf16.
 * ``ragged``     -- 10,000 one-dimensional tensors with log-uniform sizes in
   [64, 2^22], D = 16, fp32 gradients with a shared 1% exact-zero mask (the
   fp32 reduce dtype of the Part 8 page's "Mixed Precision" section).
@@ -80,6 +83,8 @@ class Workload:
     units: Tuple[Unit, ...]
     ranks: Tuple[int, ...]     # ranks whose shard is stepped and checked
     description: str
+    replicas: int = 1          # HYBRID_SHARD replica groups (nodes); 1 = FULL_SHARD
+    round_reduce: bool = False  # collectives' outputs held in the reduce dtype
 
 
 def _gpt3m_unit() -> Unit:
@@ -151,6 +156,13 @@ def get(name: str) -> Workload:
         return Workload("llama70b", 4, 8, "bf16", 3, "normal", 0.0, units, (0,),
                         "LLaMA-70B shape (80 GQA blocks + root), rank-0 shard, "
                         "D=8, one bucket per unit")
+    if name == "llama7b_hybrid":
+        units = tuple(llama_block_unit(f"block{i}", 4096, 11008, 4096)
+                      for i in range(32)) + (llama_root_unit("root", 4096, 32000),)
+        return Workload("llama7b_hybrid", 6, 8, "bf16", 3, "normal", 0.0, units, (0,),
+                        "full LLaMA-7B under HYBRID_SHARD on 4 nodes x 8 GPUs: rank-0 "
+                        "shard at D=8, 4 replica groups, bf16 collectives, one bucket "
+                        "per unit", replicas=4, round_reduce=True)
     if name == "ragged":
         return Workload("ragged", 5, 16, "f32", 5, "normal", 0.01,
                         (_ragged_unit(),), (0, 15),
@@ -158,7 +170,7 @@ def get(name: str) -> Workload:
     raise KeyError(name)
 
 
-NAMES = ("gpt3m", "llama7b_block", "llama7b_full", "llama70b", "ragged")
+NAMES = ("gpt3m", "llama7b_block", "llama7b_full", "llama70b", "ragged", "llama7b_hybrid")
 
 
 def seed_for(workload_index: int, step: int, bucket: int, k: int) -> int:
