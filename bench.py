@@ -378,7 +378,7 @@ def main() -> int:
             "master_dtype": "f32", "buckets": n_launch,
         },
         "roofline": {
-            "bound": "hbm", "kernel": "adamw_vec_kernel<bf16,8>",
+            "bound": "hbm", "kernel": "adamw_vec_kernel<bf16, FlatSum<bf16, 8>>",
             "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
