@@ -331,6 +331,19 @@ def gather_unit(shards: Sequence[np.ndarray]) -> np.ndarray:
     return np.concatenate([np.asarray(s) for s in shards]) if shards else np.zeros(0, U16)
 
 
+def reshard(shards: Sequence[np.ndarray], N: int, D_new: int) -> List[np.ndarray]:
+    """Re-shard a unit of N elements from its D shards to D_new shards.
+
+    [GPT8 "Checkpointing with FSDP"]: a sharded state dict resumes only on
+    the same GPU count, while the full state dict (gathered) loads on any
+    count. Re-sharding is that full state dict's gather followed by the
+    split of a fresh wrap: gather_unit, cut to the N real elements, then
+    pack_flat at D_new (its pad is +0 again). Bits are copied unchanged.
+    """
+    flat = gather_unit(shards)[:N]
+    return pack_flat([flat], D_new)
+
+
 def unit_views(flat: np.ndarray, shapes: Sequence[Tuple[int, ...]]) -> List[np.ndarray]:
     """Per-tensor views of a gathered flat unit at the layout's offsets."""
     offsets, _, _, _ = unit_layout([int(np.prod(s, dtype=np.int64)) for s in shapes], 1)
