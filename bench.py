@@ -238,12 +238,54 @@ def configs_leg(zs, torch, W, dev, hp, launches: int):
     return res
 
 
+def reshard_ckpt_leg(zs, torch, W, dev, p, m, v, wshard, sl, D):
+    """Re-shard and shard checkpoint rates: zs_reshard of one 70B block
+    unit's fp32 master (855,654,400 elements) from D=8 to 6 shards (HBM
+    bytes = 2 x 4 B per element), then zs_shard_save / zs_shard_load of one
+    block bucket's rank state (p, m, v, w: 14 B per param) through a file
+    in the system temp directory."""
+    import tempfile
+    unit = W.get("llama70b").units[0]
+    N = unit.numel
+    S, S2 = -(-N // D), -(-N // 6)
+    src = [p[sl][:S] for _ in range(1)] + [torch.empty(S, device=dev) for _ in range(D - 1)]
+    dst = [torch.empty(S2, device=dev) for _ in range(6)]
+    zs.zs_reshard(src, N, dst)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        zs.zs_reshard(src, N, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    res = {"reshard_block_unit_f32_8_to_6": {"elements": N, "ms": ms,
+                                              "GB_s": 8 * N / (ms / 1e3) / 1e9}}
+    del src, dst
+    torch.cuda.empty_cache()
+    Sb = sl.stop - sl.start
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "rank0.zss")
+        t0 = time.perf_counter()
+        zs.zs_shard_save(path, 0, D, Sb * D, 1, p[sl], m[sl], v[sl], wshard[sl])
+        t_save = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        zs.zs_shard_load(path, p[sl], m[sl], v[sl], wshard[sl])
+        t_load = time.perf_counter() - t0
+    res["checkpoint_one_bucket"] = {"bytes": 14 * Sb, "save_s": t_save, "load_s": t_load,
+                                    "save_GB_s": 14 * Sb / t_save / 1e9,
+                                    "load_GB_s": 14 * Sb / t_load / 1e9}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ckpt", action="store_true",
+                    help="skip the re-shard and shard checkpoint leg")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the fused-kernel rates on the other workloads' shards")
     ap.add_argument("--no-hybrid", action="store_true",
@@ -412,6 +454,10 @@ def main() -> int:
         log("pipeline leg: contributions streamed per bucket, overlapped with the step")
         out["pipeline"] = pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D,
                                        args.warmup + K + 1, hp, host_buckets=16)
+    if not args.no_ckpt:
+        log("re-shard and checkpoint leg")
+        out["reshard_checkpoint"] = reshard_ckpt_leg(zs, torch, W, dev, p, m, v, wshard,
+                                                     buckets[0][0], D)
     if not args.no_hybrid:
         log("hybrid leg: LLaMA-7B rank shard under HYBRID_SHARD, 4 x 8 contributions")
         out["hybrid_shard"] = hybrid_leg(zs, torch, W, dev, hp, steps=3)

@@ -18,7 +18,7 @@ from typing import List, Sequence, Tuple
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libzs.so")
 
-ZS_OK, ZS_EINVAL, ZS_EALIAS, ZS_EHIP, ZS_EUNSUPPORTED = 0, 1, 2, 3, 4
+ZS_OK, ZS_EINVAL, ZS_EALIAS, ZS_EHIP, ZS_EUNSUPPORTED, ZS_EIO = 0, 1, 2, 3, 4, 5
 ZS_BF16, ZS_F32 = 1, 2
 ZS_MAX_D = 64
 
@@ -42,6 +42,14 @@ class zs_bucket(ctypes.Structure):
 
 class zs_reduce_opts(ctypes.Structure):
     _fields_ = [("replicas", ctypes.c_int32), ("round_to_reduce_dtype", ctypes.c_int32)]
+
+
+class zs_shard_info(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("D", ctypes.c_int32), ("N", ctypes.c_int64),
+                ("S", ctypes.c_int64), ("step", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return dict(rank=self.rank, D=self.D, N=self.N, S=self.S, step=self.step)
 
 
 class zs_adamw_hp(ctypes.Structure):
@@ -86,6 +94,13 @@ def load() -> ctypes.CDLL:
                 "zs_adamw_step_ex": (i32, [vp, vp, vp, vp, i64, P(vp), i32, P(zs_reduce_opts),
                                            i32, P(zs_adamw_hp), vp]),
                 "zs_gather_unit": (i32, [P(vp), i32, i64, i32, vp, vp]),
+                "zs_reshard": (i32, [P(vp), i32, i64, i64, i32, P(vp), i32, i64, vp]),
+                "zs_shard_save": (i32, [ctypes.c_char_p, P(zs_shard_info), vp, vp, vp, vp, vp]),
+                "zs_shard_info_read": (i32, [ctypes.c_char_p, P(zs_shard_info)]),
+                "zs_shard_load": (i32, [ctypes.c_char_p, vp, vp, vp, vp, i64, P(zs_shard_info),
+                                        vp]),
+                "zs_shard_load_resharded": (i32, [P(ctypes.c_char_p), i32, i32, i32, vp, vp, vp,
+                                                  vp, i64, P(zs_shard_info), vp]),
                 "zs_step_pipelined": (i32, [P(zs_bucket), i32, i32, i32, vp, vp, i64,
                                             P(zs_adamw_hp), vp, vp]),
                 "zs_last_error": (ctypes.c_char_p, []),
@@ -350,6 +365,74 @@ def zs_step_pipelined(buckets: Sequence, staging: Sequence, hp, compute=None,
                                     ctypes.c_void_p(s0.data_ptr()), ctypes.c_void_p(s1.data_ptr()),
                                     staging_len, ctypes.byref(h), _stream(s0, compute),
                                     _stream(s0, transfer)))
+
+
+def zs_reshard(src: Sequence, N: int, dst: Sequence, stream=None) -> None:
+    """Re-shard a unit of N elements from shards src (D tensors of ceil(N/D))
+    to shards dst (D2 tensors of ceil(N/D2)), bits copied, new pad +0."""
+    if not src or not dst:
+        raise ValueError("need at least one source and one destination shard")
+    S, S2 = src[0].numel(), dst[0].numel()
+    code = _dtype_code(src[0])
+    for i, t in enumerate(list(src) + list(dst)):
+        _dev(t, f"shard {i}")
+        if _dtype_code(t) != code or t.element_size() != src[0].element_size():
+            raise TypeError("all shards must share one element type")
+    if any(t.numel() != S for t in src) or any(t.numel() != S2 for t in dst):
+        raise ValueError("shards of one side must have equal lengths")
+    _check(load().zs_reshard(_ptr_array(src), len(src), S, int(N), code, _ptr_array(dst),
+                             len(dst), S2, _stream(dst[0], stream)))
+
+
+def _state(p, m, v, w, S=None):
+    torch = _torch()
+    S = p.numel() if S is None else S
+    for name, t in (("p", p), ("m", m), ("v", v)):
+        _dev(t, name)
+        if t.dtype != torch.float32 or t.numel() != S:
+            raise ValueError(f"{name} must be float32 with S = {S} elements")
+    _dev(w, "w")
+    if _dtype_code(w) != ZS_BF16 or w.numel() != S:
+        raise ValueError("w must be bf16 bits with S elements")
+    return [ctypes.c_void_p(t.data_ptr()) for t in (p, m, v, w)]
+
+
+def zs_shard_save(path: str, rank: int, D: int, N: int, step: int, p, m, v, w,
+                  stream=None) -> None:
+    """Save rank `rank`'s shard (of D over N elements) after `step` steps.
+    Synchronizes the stream and writes the file."""
+    S = -(-int(N) // int(D)) if D > 0 else 0
+    info = zs_shard_info(int(rank), int(D), int(N), S, int(step))
+    ptrs = _state(p, m, v, w, S)
+    _check(load().zs_shard_save(os.fsencode(path), ctypes.byref(info), *ptrs,
+                                _stream(p, stream)))
+
+
+def zs_shard_info_read(path: str) -> dict:
+    info = zs_shard_info()
+    _check(load().zs_shard_info_read(os.fsencode(path), ctypes.byref(info)))
+    return info.as_dict()
+
+
+def zs_shard_load(path: str, p, m, v, w, stream=None) -> dict:
+    """Load a shard file saved at the same D into p, m, v, w; returns its info."""
+    ptrs = _state(p, m, v, w)
+    info = zs_shard_info()
+    _check(load().zs_shard_load(os.fsencode(path), *ptrs, p.numel(), ctypes.byref(info),
+                                _stream(p, stream)))
+    return info.as_dict()
+
+
+def zs_shard_load_resharded(paths: Sequence[str], rank: int, D2: int, p, m, v, w,
+                            stream=None) -> dict:
+    """Load rank `rank` of a D2-way sharding from the len(paths) files of one
+    checkpoint (paths[r] = rank r's file); returns the new rank's info."""
+    ptrs = _state(p, m, v, w)
+    arr = (ctypes.c_char_p * max(1, len(paths)))(*[os.fsencode(x) for x in paths])
+    info = zs_shard_info()
+    _check(load().zs_shard_load_resharded(arr, len(paths), int(rank), int(D2), *ptrs, p.numel(),
+                                          ctypes.byref(info), _stream(p, stream)))
+    return info.as_dict()
 
 
 # Raw-pointer forms, for callers that manage device memory themselves.

@@ -133,7 +133,7 @@ using namespace zs;
 
 ZS_EXPORT const char* zs_last_error(void) { return g_last_error.c_str(); }
 
-ZS_EXPORT int32_t zs_abi_version(void) { return 102; }
+ZS_EXPORT int32_t zs_abi_version(void) { return 103; }
 
 ZS_EXPORT zs_status zs_unit_layout(const int64_t* numels, int32_t T, int32_t D,
                                    int64_t* offsets_out, int64_t* n_out, int64_t* n_pad_out,
@@ -348,4 +348,37 @@ ZS_EXPORT zs_status zs_gather_unit(const void* const* shards, int32_t D, int64_t
         if (overlap(out, range_of(sp.p[r], S, es)))
             return fail(ZS_EALIAS, "zs_gather_unit: flat_out overlaps shard %d", r);
     return hip_status(launch_gather(sp, D, S, es, flat_out, stream), "zs_gather_unit launch");
+}
+
+ZS_EXPORT zs_status zs_reshard(const void* const* src, int32_t D, int64_t S, int64_t N,
+                               int32_t dtype, void* const* dst, int32_t D2, int64_t S2,
+                               hipStream_t stream) {
+    const char* who = "zs_reshard";
+    const int es = elem_size(dtype);
+    if (es == 0) return fail(ZS_EUNSUPPORTED, "%s: unknown dtype %d", who, dtype);
+    if (D < 1 || D > ZS_MAX_D || D2 < 1 || D2 > ZS_MAX_D)
+        return fail(ZS_EINVAL, "%s: D = %d, D2 = %d outside 1..%d", who, D, D2, ZS_MAX_D);
+    if (N < 0 || N > INT64_MAX / 16 / es)
+        return fail(ZS_EINVAL, "%s: N = %lld out of range", who, (long long)N);
+    const int64_t want_S = N / D + (N % D != 0 ? 1 : 0);
+    const int64_t want_S2 = N / D2 + (N % D2 != 0 ? 1 : 0);
+    if (S != want_S || S2 != want_S2)
+        return fail(ZS_EINVAL, "%s: S = %lld, S2 = %lld but ceil(N/D) = %lld, ceil(N/D2) = %lld", who,
+                    (long long)S, (long long)S2, (long long)want_S, (long long)want_S2);
+    if (N == 0) return ok();
+    PtrPack sp, dp;
+    zs_status st = take_ptrs(src, D, es, "zs_reshard: src", &sp);
+    if (st != ZS_OK) return st;
+    st = take_ptrs(const_cast<const void* const*>(dst), D2, es, "zs_reshard: dst", &dp);
+    if (st != ZS_OK) return st;
+    for (int a = 0; a < D2; ++a) {
+        const Range ra = range_of(dp.p[a], S2, es);
+        for (int b = a + 1; b < D2; ++b)
+            if (overlap(ra, range_of(dp.p[b], S2, es)))
+                return fail(ZS_EALIAS, "%s: dst shards %d and %d overlap", who, a, b);
+        for (int r = 0; r < D; ++r)
+            if (overlap(ra, range_of(sp.p[r], S, es)))
+                return fail(ZS_EALIAS, "%s: dst shard %d overlaps src shard %d", who, a, r);
+    }
+    return hip_status(launch_reshard(sp, S, dp, D2, S2, N, es, stream), "zs_reshard launch");
 }

@@ -61,5 +61,7 @@ hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es,
                        int D, const PtrPack& shards, int64_t S, hipStream_t stream);
 hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es,
                          void* flat, hipStream_t stream);
+hipError_t launch_reshard(const PtrPack& src, int64_t S, const PtrPack& dst, int D2, int64_t S2,
+                          int64_t N, int es, hipStream_t stream);
 
 }  // namespace zs

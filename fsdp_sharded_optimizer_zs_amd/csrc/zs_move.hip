@@ -1,4 +1,5 @@
-// Pack (flat unit -> D shards) and gather (D shards -> flat unit) for gfx950.
+// Pack (flat unit -> D shards), gather (D shards -> flat unit) and re-shard
+// (D shards -> D' shards of the same unit) for gfx950.
 //
 // Both are bit copies bound by HBM bandwidth. Work is split into runs that
 // are contiguous on both sides (a tensor piece that lands inside one shard,
@@ -129,7 +130,51 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(PtrPack shards, int64_
                  int64_t(blockIdx.x) * kThreads + threadIdx.x, int64_t(gridDim.x) * kThreads);
 }
 
+// Re-shard: work item q covers new-flat [lo, hi) inside new shard r2 =
+// q / per_shard. Flat position i < N comes from old shard i / S at i % S;
+// positions at or past N are the new pad and get +0.
+template <int ES>
+__global__ __launch_bounds__(kThreads) void reshard_kernel(PtrPack src, int64_t S, PtrPack dst,
+                                                           int64_t S2, int64_t N,
+                                                           int64_t per_shard, int64_t items) {
+    using Tv = typename Elem<ES>::T;
+    for (int64_t q = blockIdx.x; q < items; q += gridDim.x) {
+        const int64_t r2 = q / per_shard;
+        const int64_t base2 = r2 * S2;
+        const int64_t lo = base2 + (q - r2 * per_shard) * kPackChunk;
+        const int64_t hi = lo + kPackChunk < base2 + S2 ? lo + kPackChunk : base2 + S2;
+        char* d = static_cast<char*>(const_cast<void*>(dst.p[r2]));
+        const int64_t real_end = hi < N ? hi : N;
+        for (int64_t i = lo; i < real_end;) {
+            const int64_t r = i / S;
+            const int64_t piece_end = (r + 1) * S < real_end ? (r + 1) * S : real_end;
+            copy_run<ES>(d + (i - base2) * ES, static_cast<const char*>(src.p[r]) + (i - r * S) * ES,
+                         piece_end - i, threadIdx.x, kThreads);
+            i = piece_end;
+        }
+        const int64_t z0 = N > lo ? N : lo;
+        for (int64_t e = z0 + threadIdx.x; e < hi; e += kThreads)
+            reinterpret_cast<Tv*>(d)[e - base2] = Tv(0);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_reshard(const PtrPack& src, int64_t S, const PtrPack& dst, int D2, int64_t S2,
+                          int64_t N, int es, hipStream_t stream) {
+    const int64_t per_shard = (S2 + kPackChunk - 1) / kPackChunk;
+    const int64_t items = per_shard * D2;
+    int64_t blocks = int64_t(device_info().cu_count) * ZS_MOVE_BLOCKS_PER_CU;
+    if (blocks > items) blocks = items;
+    if (blocks < 1) blocks = 1;
+    if (es == 2)
+        hipLaunchKernelGGL((reshard_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                           src, S, dst, S2, N, per_shard, items);
+    else
+        hipLaunchKernelGGL((reshard_kernel<4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                           src, S, dst, S2, N, per_shard, items);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es, int D,
                        const PtrPack& shards, int64_t S, hipStream_t stream) {

@@ -13,6 +13,9 @@
  *   zs_gather_unit   all-gather's local rebuild of a unit from its shards
  *   zs_step_pipelined  the step over a sequence of buckets, each bucket's
  *                    contribution transfer overlapped with the previous step
+ *   zs_reshard       re-shard a unit from D to D2 shards on the device
+ *   zs_shard_save, zs_shard_load, zs_shard_load_resharded, zs_shard_info_read
+ *                    per-rank shard checkpoints, resumable at any D2
  *
  * Sources (web pages, by title and section):
  *   [ZT]   "7.10 -- Fully-sharded data parallel (FSDP / ZeRO-3)", AI / ML
@@ -56,6 +59,8 @@ typedef int32_t zs_status;
 #define ZS_EALIAS        2  /* an output overlaps an input it may not        */
 #define ZS_EHIP          3  /* the HIP runtime reported an error             */
 #define ZS_EUNSUPPORTED  4  /* unknown dtype or a size beyond the limits     */
+#define ZS_EIO           5  /* a checkpoint file could not be read or written,
+                               or failed its format or checksum checks    */
 
 /* Element types. */
 #define ZS_BF16 1  /* bf16 as uint16 bit patterns (2 bytes)                   */
@@ -309,6 +314,80 @@ typedef struct {
 zs_status zs_step_pipelined(const zs_bucket* buckets, int32_t n_buckets, int32_t n_contrib,
                             int32_t dtype, void* staging0, void* staging1, int64_t staging_len,
                             const zs_adamw_hp* hp, hipStream_t compute, hipStream_t transfer);
+
+/*
+ * zs_reshard -- re-shard one unit from D shards to D2 shards, on the device.
+ *
+ * [GPT8] "Checkpointing with FSDP": a sharded state dict resumes only on
+ * the same GPU count, while the full (gathered) state dict loads on any
+ * count. This is the full state dict's gather followed by a fresh split,
+ * in one pass with no flat buffer: for new rank r2 and j < S2, with
+ * i = r2 * S2 + j,
+ *   dst[r2][j] = src[i / S][i % S]   if i < N   (bit copy)
+ *   dst[r2][j] = +0                  if i >= N  (the new padding)
+ *
+ *   src   host array of D device pointers, each to S = ceil(N / D) elements
+ *   dst   host array of D2 device pointers, each to S2 = ceil(N / D2)
+ *   N     real (unpadded) elements of the unit, >= 0
+ *   dtype ZS_BF16 or ZS_F32 (2- or 4-byte elements; p, m, v and w are
+ *         re-sharded one array at a time)
+ * Errors: ZS_EINVAL (counts out of range, S or S2 not the layout's, NULLs,
+ * misalignment), ZS_EALIAS (a dst shard overlaps another dst or any src),
+ * ZS_EUNSUPPORTED.
+ */
+zs_status zs_reshard(const void* const* src, int32_t D, int64_t S, int64_t N, int32_t dtype,
+                     void* const* dst, int32_t D2, int64_t S2, hipStream_t stream);
+
+/* Layout and step of one rank's shard checkpoint. S = ceil(N / D). */
+typedef struct {
+    int32_t rank;   /* 0 <= rank < D                      */
+    int32_t D;      /* ranks the state was sharded over   */
+    int64_t N;      /* real elements of the sharded state */
+    int64_t S;      /* elements per rank shard            */
+    int64_t step;   /* optimizer steps taken, >= 0        */
+} zs_shard_info;
+
+/*
+ * Shard checkpoints: each rank saves its own shard (p, m, v fp32 and w
+ * bf16, S elements each) to its own file -- [GPT8] "Checkpointing with
+ * FSDP", sharded state dict, and "Shared Storage for Checkpoints", where
+ * each GPU saves its shard in parallel. A checkpoint taken at D ranks loads
+ * back at D (zs_shard_load) or at any D2 (zs_shard_load_resharded), each
+ * new rank reading only the byte ranges it owns from the old files.
+ *
+ * File format (little-endian). Header page, bytes [0, 4096):
+ *   0 char[8] "ZSSHARD1"   8 uint32 version (1)   12 uint32 header bytes (4096)
+ *   16 int32 rank   20 int32 D   24 int64 N   32 int64 S   40 int64 step
+ *   48 int64 CRC block bytes (16 MiB)
+ *   56 + 48 i, i = 0..3 (p, m, v, w): char[8] name, int32 dtype (ZS_F32 or
+ *      ZS_BF16), uint32 0, uint64 data offset, uint64 data bytes, uint64 CRC
+ *      table offset, uint64 CRC blocks
+ *   4092 uint32 CRC-32C of bytes [0, 4092)
+ * then the four arrays at 4096-aligned offsets, then per array one uint32
+ * CRC-32C (Castagnoli: reflected polynomial 0x82F63B78, initial value and
+ * final xor 0xFFFFFFFF) per 16 MiB block of its data. A file is written as
+ * path + ".tmp" and
+ * renamed into place when complete.
+ *
+ * Unlike the kernel entry points these calls SYNCHRONIZE `stream` (the
+ * state must be final before it is saved, and loaded data is complete
+ * when they return), move data through a 64 MiB pinned host buffer they
+ * allocate and free, and do file IO. The state pointers are device memory.
+ * Errors: ZS_EINVAL (arguments), ZS_EALIAS (state arrays overlap), ZS_EIO
+ * (open/read/write failure, bad magic, version or header, a checksum
+ * mismatch, files that are not ranks 0..D-1 of one checkpoint), ZS_EHIP.
+ */
+zs_status zs_shard_save(const char* path, const zs_shard_info* info, const float* p,
+                        const float* m, const float* v, const uint16_t* w, hipStream_t stream);
+zs_status zs_shard_info_read(const char* path, zs_shard_info* info);
+zs_status zs_shard_load(const char* path, float* p, float* m, float* v, uint16_t* w, int64_t S,
+                        zs_shard_info* info_out, hipStream_t stream);
+/* paths: host array of D file names, paths[r] = rank r's file of one
+ * checkpoint; fills rank `rank` of a D2-way sharding (S2 = ceil(N / D2)),
+ * the new padding +0; info_out (may be NULL) gets rank, D2, N, S2, step. */
+zs_status zs_shard_load_resharded(const char* const* paths, int32_t D, int32_t rank, int32_t D2,
+                                  float* p, float* m, float* v, uint16_t* w, int64_t S2,
+                                  zs_shard_info* info_out, hipStream_t stream);
 
 /* Text of the calling thread's most recent failure ("" if none). The pointer
  * stays valid until the thread's next call into the library. */

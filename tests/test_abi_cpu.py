@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("zs_unit_layout", "zs_pack_flat", "zs_reduce_shard", "zs_adamw_step",
               "zs_gather_unit", "zs_step_pipelined", "zs_reduce_shard_ex", "zs_adamw_step_ex",
-              "zs_last_error", "zs_abi_version"):
+              "zs_reshard", "zs_shard_save", "zs_shard_info_read", "zs_shard_load",
+              "zs_shard_load_resharded", "zs_last_error", "zs_abi_version"):
         assert n in names
 
 
@@ -266,3 +267,95 @@ def test_hybrid_argument_errors(lib):
     assert red(4, 2, 1, out=None) == zs.ZS_EINVAL
     assert red(4, 2, 1, out=cs[5] + 8) == zs.ZS_EALIAS
     assert lib.zs_reduce_shard_ex(arr, 8, None, zs.ZS_BF16, 0, None, None) == zs.ZS_OK
+
+
+def test_reshard_argument_errors(lib):
+    _no_gpu()
+    src = (ctypes.c_void_p * 4)(A, A + 0x1000, A + 0x2000, A + 0x3000)
+    dst = (ctypes.c_void_p * 3)(A + 0x10000, A + 0x11000, A + 0x12000)
+    f = lib.zs_reshard
+    assert f(src, 4, 10, 40, 7, dst, 3, 14, None) == zs.ZS_EUNSUPPORTED
+    assert f(src, 0, 10, 40, zs.ZS_F32, dst, 3, 14, None) == zs.ZS_EINVAL
+    assert f(src, 4, 10, 40, zs.ZS_F32, dst, 65, 14, None) == zs.ZS_EINVAL
+    assert f(src, 4, 11, 40, zs.ZS_F32, dst, 3, 14, None) == zs.ZS_EINVAL      # S != ceil(40/4)
+    assert f(src, 4, 10, 40, zs.ZS_F32, dst, 3, 13, None) == zs.ZS_EINVAL      # S2 != ceil(40/3)
+    assert f(src, 4, 10, -1, zs.ZS_F32, dst, 3, 14, None) == zs.ZS_EINVAL
+    dst[1] = A + 0x2008                                                         # over src shard 2
+    assert f(src, 4, 10, 40, zs.ZS_F32, dst, 3, 14, None) == zs.ZS_EALIAS
+    dst[1] = A + 0x10010                                                        # over dst shard 0
+    assert f(src, 4, 10, 40, zs.ZS_F32, dst, 3, 14, None) == zs.ZS_EALIAS
+    dst[1] = A + 0x11001
+    assert f(src, 4, 10, 40, zs.ZS_F32, dst, 3, 14, None) == zs.ZS_EINVAL      # misaligned
+    assert f(src, 4, 0, 0, zs.ZS_F32, dst, 3, 0, None) == zs.ZS_OK              # empty unit
+
+
+# -------------------------------------------------------- shard file format
+def crc32c_ref(data: bytes) -> int:
+    """CRC-32C from its definition: reflected polynomial 0x82F63B78, initial
+    value and final xor 0xFFFFFFFF, one bit at a time."""
+    c = 0xFFFFFFFF
+    for byte in data:
+        c ^= byte
+        for _ in range(8):
+            c = (c >> 1) ^ (0x82F63B78 if c & 1 else 0)
+    return c ^ 0xFFFFFFFF
+
+
+def test_crc32c_reference_check_value():
+    assert crc32c_ref(b"123456789") == 0xE3069283     # the standard check value
+
+
+def write_header_file(path, rank, D, N, step, corrupt=None):
+    """A shard file header exactly as include/zs.h documents it (no data)."""
+    import struct
+    S = -(-N // D)
+    page = bytearray(4096)
+    struct.pack_into("<8sIIiiqqqq", page, 0, b"ZSSHARD1", 1, 4096, rank, D, N, S, step, 16 << 20)
+    off = 4096
+    recs = []
+    for name, es, dtype in ((b"p", 4, 2), (b"m", 4, 2), (b"v", 4, 2), (b"w", 2, 1)):
+        nb = S * es
+        recs.append([name, dtype, off, nb, -(-nb // (16 << 20))])
+        off = -(-(off + nb) // 4096) * 4096
+    for r in recs:
+        r.insert(4, off)
+        off += r[5] * 4
+    for i, (name, dtype, doff, nb, coff, nblk) in enumerate(recs):
+        struct.pack_into("<8siIQQQQ", page, 56 + 48 * i, name, dtype, 0, doff, nb, coff, nblk)
+    struct.pack_into("<I", page, 4092, crc32c_ref(bytes(page[:4092])))
+    if corrupt is not None:
+        page[corrupt] ^= 0x01
+    with open(path, "wb") as f:
+        f.write(bytes(page))
+
+
+def test_shard_info_read_of_the_documented_format(lib, tmp_path):
+    p = str(tmp_path / "r1.zss")
+    write_header_file(p, 1, 4, 1003, 17)
+    info = zs.zs_shard_info_read(p)
+    assert info == dict(rank=1, D=4, N=1003, S=251, step=17)
+    for byte in (0, 9, 20, 30, 60, 100, 4092):
+        write_header_file(p, 1, 4, 1003, 17, corrupt=byte)
+        with pytest.raises(zs.ZsError) as e:
+            zs.zs_shard_info_read(p)
+        assert e.value.status == zs.ZS_EIO
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_shard_info_read(str(tmp_path / "missing.zss"))
+    assert e.value.status == zs.ZS_EIO
+
+
+def test_shard_save_and_load_argument_errors(lib, tmp_path):
+    _no_gpu()
+    p = str(tmp_path / "x.zss").encode()
+    info = B.zs_shard_info(0, 4, 1000, 250, 3)
+    st = lambda i, pp=A: lib.zs_shard_save(p, ctypes.byref(i), pp, pp + 0x1000, pp + 0x2000, pp + 0x3000, None)
+    assert st(B.zs_shard_info(4, 4, 1000, 250, 3)) == zs.ZS_EINVAL     # rank >= D
+    assert st(B.zs_shard_info(0, 4, 1000, 251, 3)) == zs.ZS_EINVAL     # S != ceil(N/D)
+    assert st(B.zs_shard_info(0, 4, 1000, 250, -1)) == zs.ZS_EINVAL    # negative step
+    assert st(info, pp=0) == zs.ZS_EINVAL                              # NULL state
+    assert lib.zs_shard_save(p, ctypes.byref(info), A, A + 0x40, A + 0x2000, A + 0x3000,
+                             None) == zs.ZS_EALIAS
+    assert not os.path.exists(p.decode()) and not os.path.exists(p.decode() + ".tmp")
+    arr = (ctypes.c_char_p * 1)(p)
+    assert lib.zs_shard_load_resharded(arr, 1, 2, 2, A, A + 0x1000, A + 0x2000, A + 0x3000, 10,
+                                       None, None) == zs.ZS_EINVAL   # rank >= D2
