@@ -278,12 +278,75 @@ def reshard_ckpt_leg(zs, torch, W, dev, p, m, v, wshard, sl, D):
     return res
 
 
+def offload_leg(zs, torch, W, dev, hp, threads: int):
+    """ZeRO-Offload on the full LLaMA-7B rank shard at D=32 (the CPU-offload
+    example of the 7.10 page: ~100 ms/step extra over ~50 GB/s PCIe): p, m, v
+    in pinned host memory, 32 bf16 contributions on the device. Times one
+    zs_offload_step (device reduce, gradient down, host AdamW, working shard
+    up) and, apart, the host AdamW alone and the two transfers alone."""
+    w = W.get("llama7b_full")
+    D = w.D
+    S = int(sum(zs.zs_unit_layout(u.numels, D)[3] for u in w.units))
+    cs = [W.contribution(w, S, 1, 0, k, dev) for k in range(D)]
+    pin = dict(pin_memory=True)
+    ph = torch.empty(S, dtype=torch.float32, **pin)
+    ph.copy_(W.master_init(S, 7100, dev))
+    mh = torch.zeros(S, dtype=torch.float32, **pin)
+    vh = torch.zeros(S, dtype=torch.float32, **pin)
+    gh = torch.empty(S, dtype=torch.float32, **pin)
+    wh = torch.empty(S, dtype=torch.int16, **pin)
+    gdev = torch.empty(S, device=dev)
+    wdev = torch.empty(S, dtype=torch.int16, device=dev)
+    stream, h2d = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+
+    def step(t):
+        zs.zs_offload_step(cs, gdev, gh, ph, mh, vh, wh, wdev, dict(step=t, **hp),
+                           threads=threads, chunk=1 << 24, stream=stream, h2d_stream=h2d)
+        h2d.synchronize()
+        stream.synchronize()
+
+    step(1)
+    t0 = time.perf_counter()
+    for t in range(2, 5):
+        step(t)
+    t_step = (time.perf_counter() - t0) / 3
+    t0 = time.perf_counter()
+    for t in range(5, 8):
+        zs.zs_adamw_step_host(ph, mh, vh, wh, gh, dict(step=t, **hp), threads=threads)
+    t_host = (time.perf_counter() - t0) / 3
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    with torch.cuda.stream(stream):
+        e[0].record()
+        gh.copy_(gdev, non_blocking=True)
+        e[1].record()
+        e[2].record()
+        wdev.copy_(wh, non_blocking=True)
+        e[3].record()
+    torch.cuda.synchronize()
+    d2h, h2d_ms = e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3])
+    res = {"workload": "full LLaMA-7B, rank-0 shard at D=32 (32 bf16 contributions)",
+           "shard_params": S, "threads": threads,
+           "offload_step_ms": t_step * 1e3,
+           "host_adamw_ms": t_host * 1e3, "host_adamw_params_per_s": S / t_host,
+           "host_adamw_GB_s": 30 * S / t_host / 1e9,
+           "grad_d2h_ms": d2h, "grad_d2h_GB_s": 4 * S / (d2h / 1e3) / 1e9,
+           "weights_h2d_ms": h2d_ms, "weights_h2d_GB_s": 2 * S / (h2d_ms / 1e3) / 1e9}
+    del cs, ph, mh, vh, gh, wh, gdev, wdev
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the ZeRO-Offload (host-core AdamW) leg")
+    ap.add_argument("--host-threads", type=int, default=16,
+                    help="host threads for the offload leg (the GPU box's CPU share)")
     ap.add_argument("--no-ckpt", action="store_true",
                     help="skip the re-shard and shard checkpoint leg")
     ap.add_argument("--no-configs", action="store_true",
@@ -458,6 +521,9 @@ def main() -> int:
         log("re-shard and checkpoint leg")
         out["reshard_checkpoint"] = reshard_ckpt_leg(zs, torch, W, dev, p, m, v, wshard,
                                                      buckets[0][0], D)
+    if not args.no_offload:
+        log("offload leg: LLaMA-7B D=32 rank shard, AdamW on host cores")
+        out["offload"] = offload_leg(zs, torch, W, dev, hp, args.host_threads)
     if not args.no_hybrid:
         log("hybrid leg: LLaMA-7B rank shard under HYBRID_SHARD, 4 x 8 contributions")
         out["hybrid_shard"] = hybrid_leg(zs, torch, W, dev, hp, steps=3)

@@ -95,6 +95,9 @@ def load() -> ctypes.CDLL:
                                            i32, P(zs_adamw_hp), vp]),
                 "zs_gather_unit": (i32, [P(vp), i32, i64, i32, vp, vp]),
                 "zs_reshard": (i32, [P(vp), i32, i64, i64, i32, P(vp), i32, i64, vp]),
+                "zs_adamw_step_host": (i32, [vp, vp, vp, vp, i64, vp, P(zs_adamw_hp), i32]),
+                "zs_offload_step": (i32, [P(vp), i32, i32, i64, vp, vp, vp, vp, vp, vp, vp,
+                                          P(zs_adamw_hp), i32, i64, vp, vp]),
                 "zs_shard_save": (i32, [ctypes.c_char_p, P(zs_shard_info), vp, vp, vp, vp, vp]),
                 "zs_shard_info_read": (i32, [ctypes.c_char_p, P(zs_shard_info)]),
                 "zs_shard_load": (i32, [ctypes.c_char_p, vp, vp, vp, vp, i64, P(zs_shard_info),
@@ -433,6 +436,55 @@ def zs_shard_load_resharded(paths: Sequence[str], rank: int, D2: int, p, m, v, w
     _check(load().zs_shard_load_resharded(arr, len(paths), int(rank), int(D2), *ptrs, p.numel(),
                                           ctypes.byref(info), _stream(p, stream)))
     return info.as_dict()
+
+
+def _host_f32(t, name, S):
+    torch = _torch()
+    if t.is_cuda or t.dtype != torch.float32 or t.numel() != S or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous host float32 tensor of {S} elements")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _host_bf16(t, name, S):
+    if t.is_cuda or _dtype_code(t) != ZS_BF16 or t.numel() != S or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous host bf16-bits tensor of {S} elements")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def zs_adamw_step_host(p, m, v, w_out, grad, hp, threads: int = 16) -> None:
+    """AdamW on host tensors (p, m, v in place, w_out written) from the
+    reduced fp32 gradient, on `threads` host threads."""
+    S = p.numel()
+    args = [_host_f32(p, "p", S), _host_f32(m, "m", S), _host_f32(v, "v", S),
+            _host_bf16(w_out, "w_out", S)]
+    h = _hp(hp)
+    _check(load().zs_adamw_step_host(*args, S, _host_f32(grad, "grad", S), ctypes.byref(h),
+                                     int(threads)))
+
+
+def zs_offload_step(contribs: Sequence, grad_dev, grad_host, p, m, v, w_host, w_dev, hp,
+                    threads: int = 16, chunk: int = 1 << 24, stream=None, h2d_stream=None) -> None:
+    """One ZeRO-Offload shard step: device reduce, gradient down in chunks,
+    host AdamW per chunk, working shard up on h2d_stream."""
+    S = p.numel()
+    code = _dtype_code(contribs[0]) if contribs else ZS_F32
+    for i, c in enumerate(contribs):
+        _dev(c, f"contribs[{i}]")
+        if c.numel() != S or _dtype_code(c) != code:
+            raise ValueError("contributions must share one dtype and hold S elements")
+    _dev(grad_dev, "grad_dev")
+    _dev(w_dev, "w_dev")
+    if grad_dev.dtype != _torch().float32 or grad_dev.numel() != S:
+        raise ValueError("grad_dev must be float32 with S elements")
+    if _dtype_code(w_dev) != ZS_BF16 or w_dev.numel() != S:
+        raise ValueError("w_dev must be bf16 bits with S elements")
+    h = _hp(hp)
+    _check(load().zs_offload_step(
+        _ptr_array(contribs), len(contribs), code, S, ctypes.c_void_p(grad_dev.data_ptr()),
+        _host_f32(grad_host, "grad_host", S), _host_f32(p, "p", S), _host_f32(m, "m", S),
+        _host_f32(v, "v", S), _host_bf16(w_host, "w_host", S), ctypes.c_void_p(w_dev.data_ptr()),
+        ctypes.byref(h), int(threads), int(chunk), _stream(grad_dev, stream),
+        _stream(grad_dev, h2d_stream)))
 
 
 # Raw-pointer forms, for callers that manage device memory themselves.

@@ -133,7 +133,7 @@ using namespace zs;
 
 ZS_EXPORT const char* zs_last_error(void) { return g_last_error.c_str(); }
 
-ZS_EXPORT int32_t zs_abi_version(void) { return 103; }
+ZS_EXPORT int32_t zs_abi_version(void) { return 104; }
 
 ZS_EXPORT zs_status zs_unit_layout(const int64_t* numels, int32_t T, int32_t D,
                                    int64_t* offsets_out, int64_t* n_out, int64_t* n_pad_out,

@@ -16,6 +16,8 @@
  *   zs_reshard       re-shard a unit from D to D2 shards on the device
  *   zs_shard_save, zs_shard_load, zs_shard_load_resharded, zs_shard_info_read
  *                    per-rank shard checkpoints, resumable at any D2
+ *   zs_adamw_step_host, zs_offload_step
+ *                    the step's AdamW on host cores (ZeRO-Offload)
  *
  * Sources (web pages, by title and section):
  *   [ZT]   "7.10 -- Fully-sharded data parallel (FSDP / ZeRO-3)", AI / ML
@@ -388,6 +390,58 @@ zs_status zs_shard_load(const char* path, float* p, float* m, float* v, uint16_t
 zs_status zs_shard_load_resharded(const char* const* paths, int32_t D, int32_t rank, int32_t D2,
                                   float* p, float* m, float* v, uint16_t* w, int64_t S2,
                                   zs_shard_info* info_out, hipStream_t stream);
+
+/*
+ * zs_adamw_step_host -- the AdamW update of zs_adamw_step on HOST memory,
+ * on host cores (ZeRO-Offload's optimizer step).
+ *
+ * [ZT] section 8: the Adam optimizer state moves to CPU memory; each step
+ * the gradients go to the CPU and the updated weights come back. This is
+ * that CPU step: for i < S, with g = grad[i] (the reduced fp32 gradient, as
+ * zs_reduce_shard writes it), exactly the operations of zs_adamw_step with
+ * one fp32 contribution, in the same order and rounding, so the results are
+ * bit-identical to the device step. Runs synchronously on `threads` host
+ * threads (the calling thread is one of them), vectorized with AVX2 where
+ * the CPU has it; denormals are kept whatever the caller's MXCSR.
+ *
+ *   p, m, v  host, S floats, updated in place;  w_out host, S bf16, written
+ *   grad     host, S floats, read
+ *   threads  1..1024
+ * Errors: ZS_EINVAL (NULLs, misalignment, threads, hyperparameters),
+ * ZS_EALIAS (any two of p, m, v, w_out, grad overlap).
+ */
+zs_status zs_adamw_step_host(float* p, float* m, float* v, uint16_t* w_out, int64_t S,
+                             const float* grad, const zs_adamw_hp* hp, int32_t threads);
+
+/*
+ * zs_offload_step -- one ZeRO-Offload shard step: reduce on the device,
+ * gradient down, AdamW on host cores, working shard up.
+ *
+ * [ZT] section 8 (cost: gradients to the CPU and weights back over PCIe
+ * every step). Enqueues the zs_reduce_shard reduce of the D device
+ * contributions into grad_dev on `stream`, then copies grad_dev to
+ * grad_host in chunks of `chunk` elements on `stream`; as each chunk lands
+ * the host steps it (zs_adamw_step_host arithmetic on p, m, v, w_host) and
+ * enqueues its copy w_host -> w_dev on `h2d_stream`. Returns when the host
+ * work is done; the last working-shard copies may still be in flight on
+ * h2d_stream (synchronize it before reading w_dev or rewriting w_host).
+ * Results are bit-identical to zs_adamw_step on the same contributions.
+ *
+ *   contribs   host array of D device pointers, S elements of dtype each
+ *   grad_dev   device, S floats (scratch, written)
+ *   grad_host  host, S floats (written; pinned memory makes the copies async)
+ *   p, m, v    host, S floats, updated in place
+ *   w_host     host, S bf16 (written; pinned for async copies)
+ *   w_dev      device, S bf16 (written by the copies)
+ *   threads    1..1024 host threads;  chunk  >= 1 elements per pipeline chunk
+ * Errors: as zs_reduce_shard and zs_adamw_step_host; ZS_EALIAS also when
+ * grad_dev and w_dev overlap each other or a contribution.
+ */
+zs_status zs_offload_step(const void* const* contribs, int32_t D, int32_t dtype, int64_t S,
+                          float* grad_dev, float* grad_host, float* p, float* m, float* v,
+                          uint16_t* w_host, uint16_t* w_dev, const zs_adamw_hp* hp,
+                          int32_t threads, int64_t chunk, hipStream_t stream,
+                          hipStream_t h2d_stream);
 
 /* Text of the calling thread's most recent failure ("" if none). The pointer
  * stays valid until the thread's next call into the library. */

@@ -1,0 +1,94 @@
+"""The host (ZeRO-Offload) AdamW step, zs_adamw_step_host, against the CPU
+oracle: bit-exact on ragged sizes, several thread counts, several steps,
+special values (zeros, signed zeros, denormal gradients and moments, huge
+and NaN values), and with the caller's FPU set to flush denormals. Runs on
+the host only: no GPU is needed."""
+import numpy as np
+import pytest
+import torch
+
+import fsdp_sharded_optimizer_zs_amd as zs
+import workloads as W
+from oracle import zs_oracle as O
+
+HP = W.ADAMW_HP
+
+
+def host_state(S, seed):
+    g = torch.Generator().manual_seed(seed)
+    p = (torch.randn(S, generator=g) * 0.02).contiguous()
+    return p, torch.zeros(S), torch.zeros(S), torch.zeros(S, dtype=torch.int16)
+
+
+def grads(S, seed, specials=False):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(S, generator=g) * 1e-3
+    if specials and S >= 16:
+        vals = torch.tensor([0.0, -0.0, 1e-40, -1e-42, 3e38, -3e38, 1e-45, 2.0 ** -126,
+                             float("nan"), 7.0, -1e-30, 1e30], dtype=torch.float32)
+        idx = torch.randint(0, S, (min(S, 4000),), generator=g)
+        x[idx] = vals[torch.randint(0, len(vals), (idx.numel(),), generator=g)]
+    return x
+
+
+def check(a, b, what):
+    a, b = np.asarray(a), np.asarray(b)
+    if a.dtype == np.float32:
+        both_nan = np.isnan(a) & np.isnan(b)
+        ne = (a.view(np.uint32) != b.view(np.uint32)) & ~both_nan
+    else:
+        ne = a.view(np.uint16) != b.view(np.uint16)
+    assert not ne.any(), f"{what}: {int(ne.sum())} elements differ, first at {np.flatnonzero(ne)[0]}"
+
+
+@pytest.mark.parametrize("S", [1, 7, 63, 64, 65, 1000, 1_000_003])
+@pytest.mark.parametrize("threads", [1, 3, 16])
+def test_host_step_matches_oracle(S, threads):
+    p, m, v, w = host_state(S, S)
+    op, om, ov = p.numpy().copy(), m.numpy().copy(), v.numpy().copy()
+    for t in (1, 2, 3):
+        g = grads(S, 100 * t + S, specials=(t == 2))
+        hp = dict(step=t, **HP)
+        zs.zs_adamw_step_host(p, m, v, w, g, hp, threads=threads)
+        with np.errstate(all="ignore"):      # the specials overflow g * g to inf
+            op, om, ov, ow = O.adamw_step(op, om, ov, g.numpy(), O.AdamWHP(**hp))
+        check(p.numpy(), op, f"p step {t}")
+        check(m.numpy(), om, f"m step {t}")
+        check(v.numpy(), ov, f"v step {t}")
+        check(w.numpy().view(np.uint16), ow, f"w step {t}")
+
+
+def test_denormals_kept_when_the_caller_flushes():
+    S = 4099
+    p, m, v, w = host_state(S, 1)
+    p[:100] = 1e-39                      # denormal parameters
+    g = grads(S, 2)
+    g[100:200] = 1e-41                   # denormal gradients: g*g underflows, m keeps them
+    op, om, ov, ow = O.adamw_step(p.numpy().copy(), m.numpy().copy(), v.numpy().copy(), g.numpy(),
+                                  O.AdamWHP(step=1, **HP))
+    assert torch.set_flush_denormal(True)
+    try:
+        zs.zs_adamw_step_host(p, m, v, w, g, dict(step=1, **HP), threads=1)
+    finally:
+        torch.set_flush_denormal(False)
+    check(p.numpy(), op, "p")
+    check(m.numpy(), om, "m")
+    check(w.numpy().view(np.uint16), ow, "w")
+    assert (np.abs(om[100:200]) > 0).all() and (np.abs(om[100:200]) < 1.2e-38).all()
+
+
+def test_host_step_argument_errors():
+    S = 100
+    p, m, v, w = host_state(S, 0)
+    g = grads(S, 1)
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_adamw_step_host(p, m, v, w, g, dict(step=1, **HP), threads=0)
+    assert e.value.status == zs.ZS_EINVAL
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_adamw_step_host(p, p, v, w, g, dict(step=1, **HP))
+    assert e.value.status == zs.ZS_EALIAS
+    with pytest.raises(zs.ZsError) as e:
+        zs.zs_adamw_step_host(p, m, v, w, g, dict(step=0, **HP))
+    assert e.value.status == zs.ZS_EINVAL
+    with pytest.raises(ValueError):
+        zs.zs_adamw_step_host(p, m, v, w, g[:50], dict(step=1, **HP))
