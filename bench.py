@@ -343,6 +343,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the no-arithmetic stream ceiling on the same buckets")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the ZeRO-Offload (host-core AdamW) leg")
     ap.add_argument("--host-threads", type=int, default=16,
@@ -455,6 +457,27 @@ def main() -> int:
     ms_per_step = elapsed * 1e3 / K
     log(f"{ms_per_step:.2f} ms/step")
 
+    # The same buckets and contributions through zs_stream_ceiling: the fused
+    # kernel's streams without its arithmetic (it overwrites p, m, v, w, which
+    # are re-initialized afterwards).
+    if not args.no_ceiling:
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_launch)]
+        for rep in range(2):
+            for i, (sl, sz, cs, _, _) in enumerate(buckets):
+                if rep:
+                    cev[i][0].record()
+                zs.zs_stream_ceiling(p[sl], m[sl], v[sl], wshard[sl], cs)
+                if rep:
+                    cev[i][1].record()
+        torch.cuda.synchronize()
+        ceiling_s = sum(a.elapsed_time(b) for a, b in cev) / 1e3 / n_launch
+        for a in range(0, S, 1 << 30):
+            b = min(S, a + (1 << 30))
+            torch.randn(b - a, generator=gen, device=dev, out=p[a:b]).mul_(W.PARAM_STD)
+        m.zero_()
+        v.zero_()
+        torch.cuda.synchronize()
+
     es = 2
     bpp = 26 + D * es                              # fused: 12 read + 14 written + D*es
     adam_launches = K * n_launch
@@ -463,6 +486,13 @@ def main() -> int:
     achieved = bytes_per_launch / adam_avg_s / 1e9
     gather_bytes = 4.0 * D * S                     # D*S bf16 read + written per step
     traffic = traffic_from_profiles()
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling_gbs = bytes_per_launch / ceiling_s / 1e9
+        ceiling = {"kernel": "zs_stream_ceiling: the same streams, launch shape and cache hints, "
+                             "no arithmetic", "avg_launch_ms": ceiling_s * 1e3,
+                   "GB_s": ceiling_gbs, "frac_of_peak": ceiling_gbs / PEAK_HBM_GBS,
+                   "fused_over_ceiling": achieved / ceiling_gbs}
     out = {
         "metric": METRIC,
         "value": S * K / elapsed,
@@ -492,6 +522,7 @@ def main() -> int:
             "algorithmic_bytes_per_param": bpp,
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "avg_launch_ms": adam_avg_s * 1e3,
+            "stream_ceiling": ceiling,
         },
         "adamw_fused": {"params_per_s": S * K / (adam_ms / 1e3),
                         "ms_per_step": adam_ms / K, "GB_s": achieved},

@@ -96,6 +96,7 @@ def load() -> ctypes.CDLL:
                 "zs_gather_unit": (i32, [P(vp), i32, i64, i32, vp, vp]),
                 "zs_reshard": (i32, [P(vp), i32, i64, i64, i32, P(vp), i32, i64, vp]),
                 "zs_adamw_step_host": (i32, [vp, vp, vp, vp, i64, vp, P(zs_adamw_hp), i32]),
+                "zs_stream_ceiling": (i32, [vp, vp, vp, vp, i64, P(vp), i32, i32, vp]),
                 "zs_offload_step": (i32, [P(vp), i32, i32, i64, vp, vp, vp, vp, vp, vp, vp,
                                           P(zs_adamw_hp), i32, i64, vp, vp]),
                 "zs_shard_save": (i32, [ctypes.c_char_p, P(zs_shard_info), vp, vp, vp, vp, vp]),
@@ -485,6 +486,20 @@ def zs_offload_step(contribs: Sequence, grad_dev, grad_host, p, m, v, w_host, w_
         _host_f32(v, "v", S), _host_bf16(w_host, "w_host", S), ctypes.c_void_p(w_dev.data_ptr()),
         ctypes.byref(h), int(threads), int(chunk), _stream(grad_dev, stream),
         _stream(grad_dev, h2d_stream)))
+
+
+def zs_stream_ceiling(p, m, v, w, contribs: Sequence, stream=None) -> None:
+    """Measurement aid: the fused step's streams without its arithmetic
+    (p, m, v, w are overwritten with placeholders)."""
+    S = p.numel()
+    ptrs = _state(p, m, v, w)
+    code = _dtype_code(contribs[0])
+    for i, c in enumerate(contribs):
+        _dev(c, f"contribs[{i}]")
+        if c.numel() != S or _dtype_code(c) != code:
+            raise ValueError("contributions must share one dtype and hold S elements")
+    _check(load().zs_stream_ceiling(*ptrs, S, _ptr_array(contribs), len(contribs), code,
+                                    _stream(p, stream)))
 
 
 # Raw-pointer forms, for callers that manage device memory themselves.

@@ -133,7 +133,7 @@ using namespace zs;
 
 ZS_EXPORT const char* zs_last_error(void) { return g_last_error.c_str(); }
 
-ZS_EXPORT int32_t zs_abi_version(void) { return 104; }
+ZS_EXPORT int32_t zs_abi_version(void) { return 105; }
 
 ZS_EXPORT zs_status zs_unit_layout(const int64_t* numels, int32_t T, int32_t D,
                                    int64_t* offsets_out, int64_t* n_out, int64_t* n_pad_out,
@@ -381,4 +381,30 @@ ZS_EXPORT zs_status zs_reshard(const void* const* src, int32_t D, int64_t S, int
                 return fail(ZS_EALIAS, "%s: dst shard %d overlaps src shard %d", who, a, r);
     }
     return hip_status(launch_reshard(sp, S, dp, D2, S2, N, es, stream), "zs_reshard launch");
+}
+
+ZS_EXPORT zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w, int64_t S,
+                                      const void* const* contribs, int32_t n, int32_t dtype,
+                                      hipStream_t stream) {
+    const char* who = "zs_stream_ceiling";
+    const int es = elem_size(dtype);
+    if (es == 0) return fail(ZS_EUNSUPPORTED, "%s: unknown dtype %d", who, dtype);
+    if (n < 1 || n > ZS_MAX_D) return fail(ZS_EINVAL, "%s: n = %d outside 1..%d", who, n, ZS_MAX_D);
+    if (!size_ok(S, 4)) return fail(ZS_EINVAL, "%s: S = %lld out of range", who, (long long)S);
+    if (S < 8) return ok();
+    if (!p || !m || !v || !w) return fail(ZS_EINVAL, "%s: p, m, v or w is NULL", who);
+    if (!aligned(p, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(w, 16))
+        return fail(ZS_EINVAL, "%s: p, m, v and w must be 16-byte aligned", who);
+    PtrPack cp;
+    zs_status st = take_ptrs(contribs, n, 16, "zs_stream_ceiling: contribs", &cp);
+    if (st != ZS_OK) return st;
+    const Range rs[4] = {range_of(p, S, 4), range_of(m, S, 4), range_of(v, S, 4), range_of(w, S, 2)};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(rs[a], rs[b])) return fail(ZS_EALIAS, "%s: outputs overlap", who);
+        for (int q = 0; q < n; ++q)
+            if (overlap(rs[a], range_of(cp.p[q], S, es)))
+                return fail(ZS_EALIAS, "%s: contribution %d overlaps an output", who, q);
+    }
+    return hip_status(launch_streams(p, m, v, w, S, cp, n, dtype, stream), who);
 }

@@ -7,6 +7,14 @@
 
 #include "../../include/zs.h"
 
+// Workgroups of 256 threads per CU for the step kernels' persistent grid:
+// 2 per CU (8 wavefronts) was the fastest setting measured on MI355X over
+// the 81 buckets of a 70B rank shard; 1, 4 and 8 per CU, 4-element lanes
+// and 512-element wave tiles were all equal or slower.
+#ifndef ZS_STEP_BLOCKS_PER_CU
+#define ZS_STEP_BLOCKS_PER_CU 2
+#endif
+
 namespace zs {
 
 // Up to ZS_MAX_D device pointers passed by value as a kernel argument.
@@ -61,6 +69,8 @@ hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es,
                        int D, const PtrPack& shards, int64_t S, hipStream_t stream);
 hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es,
                          void* flat, hipStream_t stream);
+hipError_t launch_streams(float* p, float* m, float* v, uint16_t* w, int64_t S,
+                          const PtrPack& contribs, int n, int dtype, hipStream_t stream);
 hipError_t launch_reshard(const PtrPack& src, int64_t S, const PtrPack& dst, int D2, int64_t S2,
                           int64_t N, int es, hipStream_t stream);
 

@@ -443,6 +443,20 @@ zs_status zs_offload_step(const void* const* contribs, int32_t D, int32_t dtype,
                           int32_t threads, int64_t chunk, hipStream_t stream,
                           hipStream_t h2d_stream);
 
+/*
+ * zs_stream_ceiling -- a measurement aid, not part of the step: moves the
+ * fused step's exact memory streams with none of its arithmetic (reads n
+ * contributions and p, m, v; writes p, m, v and w), with the fused kernel's
+ * launch shape, lane map and cache hints, so that the step kernel can be
+ * read against what HBM delivers for its own mix of streams. The values it
+ * writes are placeholders: p, m, v and w are garbage afterwards. Processes
+ * the first 8 * floor(S / 8) elements; every buffer 16-byte aligned.
+ * Errors: ZS_EINVAL, ZS_EALIAS, ZS_EUNSUPPORTED as zs_adamw_step.
+ */
+zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w, int64_t S,
+                            const void* const* contribs, int32_t n, int32_t dtype,
+                            hipStream_t stream);
+
 /* Text of the calling thread's most recent failure ("" if none). The pointer
  * stays valid until the thread's next call into the library. */
 const char* zs_last_error(void);

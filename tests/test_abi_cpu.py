@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     for n in ("zs_unit_layout", "zs_pack_flat", "zs_reduce_shard", "zs_adamw_step",
               "zs_gather_unit", "zs_step_pipelined", "zs_reduce_shard_ex", "zs_adamw_step_ex",
               "zs_reshard", "zs_shard_save", "zs_shard_info_read", "zs_shard_load",
-              "zs_shard_load_resharded", "zs_last_error", "zs_abi_version"):
+              "zs_shard_load_resharded", "zs_adamw_step_host", "zs_offload_step",
+              "zs_stream_ceiling", "zs_last_error", "zs_abi_version"):
         assert n in names
 
 
