@@ -6,8 +6,10 @@
 // or one shard landing in the flat unit). Lanes write whole 16-byte
 // destination vectors (dwordx4 stores); the source is read with dwordx4
 // loads when it is 16-byte aligned relative to the destination and with
-// narrower, still coalesced, loads otherwise. The few elements before the
-// first and after the last aligned vector of a run are copied one per lane.
+// narrower, still coalesced, loads otherwise; loads and stores of the
+// vector body are non-temporal (each byte is touched once). The few elements
+// before the first and after the last aligned vector of a run are copied one
+// per lane.
 // No lane ever touches a byte outside the run it copies.
 
 #include "zs_internal.h"
@@ -60,12 +62,13 @@ __device__ __forceinline__ void copy_run(char* dst, const char* src, int64_t n, 
     const uintptr_t sa = reinterpret_cast<uintptr_t>(sb);
     if ((sa & 15) == 0) {
         const u32x4* s4 = reinterpret_cast<const u32x4*>(sb);
-        for (int64_t i = tid; i < body; i += nthr) db[i] = __builtin_nontemporal_load(s4 + i);
+        for (int64_t i = tid; i < body; i += nthr)
+            __builtin_nontemporal_store(__builtin_nontemporal_load(s4 + i), db + i);
     } else if ((sa & 3) == 0) {
         const uint32_t* s1 = reinterpret_cast<const uint32_t*>(sb);
         for (int64_t i = tid; i < body; i += nthr) {
             const uint32_t* s = s1 + 4 * i;
-            db[i] = u32x4{s[0], s[1], s[2], s[3]};
+            __builtin_nontemporal_store(u32x4{s[0], s[1], s[2], s[3]}, db + i);
         }
     } else {  // 2-byte elements at an odd element offset
         const uint16_t* s1 = reinterpret_cast<const uint16_t*>(sb);
@@ -74,7 +77,7 @@ __device__ __forceinline__ void copy_run(char* dst, const char* src, int64_t n, 
             u32x4 x;
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = uint32_t(s[2 * e]) | (uint32_t(s[2 * e + 1]) << 16);
-            db[i] = x;
+            __builtin_nontemporal_store(x, db + i);
         }
     }
 }
@@ -121,13 +124,19 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const zs_tensor_ref* __r
     }
 }
 
-// Gather: blockIdx.y = shard r, copied to flat[r*S, (r+1)*S).
+// Gather: the whole grid copies shard 0 to flat[0, S), then shard 1 to
+// flat[S, 2S), and so on. Walking the shards in order keeps one read and one
+// write stream open at a time; giving each shard its own slice of the grid
+// (all D copies at once) measured 8% slower on the 70B units, 5.43 against
+// 5.87 TB/s with the non-temporal stores.
 template <int ES>
-__global__ __launch_bounds__(kThreads) void gather_kernel(PtrPack shards, int64_t S,
+__global__ __launch_bounds__(kThreads) void gather_kernel(PtrPack shards, int D, int64_t S,
                                                           char* __restrict__ flat) {
-    const int r = blockIdx.y;
-    copy_run<ES>(flat + int64_t(r) * S * ES, static_cast<const char*>(shards.p[r]), S,
-                 int64_t(blockIdx.x) * kThreads + threadIdx.x, int64_t(gridDim.x) * kThreads);
+    const int64_t tid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    const int64_t nthr = int64_t(gridDim.x) * kThreads;
+    for (int r = 0; r < D; ++r)
+        copy_run<ES>(flat + int64_t(r) * S * ES, static_cast<const char*>(shards.p[r]), S, tid,
+                     nthr);
 }
 
 // Re-shard: work item q covers new-flat [lo, hi) inside new shard r2 =
@@ -195,17 +204,17 @@ hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es, i
 hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es, void* flat,
                          hipStream_t stream) {
     const int64_t vecs = (S * es + 15) / 16 + 1;
-    int64_t bx = (vecs + kThreads - 1) / kThreads;
-    const int64_t cap = (int64_t(device_info().cu_count) * ZS_MOVE_BLOCKS_PER_CU + D - 1) / D;
-    if (bx > cap) bx = cap;
-    if (bx < 1) bx = 1;
+    int64_t blocks = (vecs + kThreads - 1) / kThreads;
+    const int64_t cap = int64_t(device_info().cu_count) * ZS_MOVE_BLOCKS_PER_CU;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
     char* f = static_cast<char*>(flat);
     if (es == 2)
-        hipLaunchKernelGGL((gather_kernel<2>), dim3(unsigned(bx), unsigned(D)), dim3(kThreads), 0,
-                           stream, shards, S, f);
+        hipLaunchKernelGGL((gather_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                           shards, D, S, f);
     else
-        hipLaunchKernelGGL((gather_kernel<4>), dim3(unsigned(bx), unsigned(D)), dim3(kThreads), 0,
-                           stream, shards, S, f);
+        hipLaunchKernelGGL((gather_kernel<4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                           shards, D, S, f);
     return hipGetLastError();
 }
 
