@@ -201,22 +201,27 @@ def hybrid_leg(zs, torch, W, dev, hp, steps: int):
     return res
 
 
-def configs_leg(zs, torch, W, dev, hp, launches: int):
+def configs_leg(zs, torch, W, dev, hp, launches: int, arenas):
     """The fused reduce + AdamW kernel alone on the rank shards of the other
     workloads (one launch over each whole shard, contributions resident):
     3.3M GPT at D=4, one LLaMA-7B block at D=8, the full LLaMA-7B at D=32
     (Student-t gradients) and the 10,000-tensor ragged unit at D=16 with fp32
     contributions. Reports the average launch time and HBM GB/s at the
-    algorithmic 26 + D * es bytes per param."""
+    algorithmic 26 + D * es bytes per param. Each shard's p, m, v (and w) are
+    placed at the start of the 70B run's own four state arrays (`arenas`,
+    re-initialized here), so that they sit tens of GB apart in HBM as a
+    rank's separately allocated state arrays do; allocated back to back they
+    run 10-15% slower."""
     res = {}
+    P, M, V, WS = arenas
     for name in ("gpt3m", "llama7b_block", "llama7b_full", "ragged"):
         w = W.get(name)
         S = int(sum(zs.zs_unit_layout(u.numels, w.D)[3] for u in w.units))
         es = 2 if w.reduce_dtype == "bf16" else 4
-        p = W.master_init(S, 7000 + w.index, dev)
-        m = torch.zeros(S, device=dev)
-        v = torch.zeros(S, device=dev)
-        ws = torch.empty(S, dtype=torch.int16, device=dev)
+        p, m, v, ws = P[:S], M[:S], V[:S], WS[:S]
+        p.copy_(W.master_init(S, 7000 + w.index, dev))
+        m.zero_()
+        v.zero_()
         mask = W.step_mask(w, S, 1, 0, dev)
         cs = [W.contribution(w, S, 1, 0, k, dev, mask) for k in range(w.D)]
         del mask
@@ -233,7 +238,7 @@ def configs_leg(zs, torch, W, dev, hp, launches: int):
         res[name] = {"shard_params": S, "D": w.D, "reduce_dtype": w.reduce_dtype,
                      "bytes_per_param": bpp, "launch_ms": ms,
                      "params_per_s": S / (ms / 1e3), "GB_s": bpp * S / (ms / 1e3) / 1e9}
-        del p, m, v, ws, cs
+        del cs
         torch.cuda.empty_cache()
     return res
 
@@ -560,7 +565,8 @@ def main() -> int:
         out["hybrid_shard"] = hybrid_leg(zs, torch, W, dev, hp, steps=3)
     if not args.no_configs:
         log("configs leg: the fused kernel on the other workloads' rank shards")
-        out["other_workloads"] = configs_leg(zs, torch, W, dev, hp, launches=10)
+        out["other_workloads"] = configs_leg(zs, torch, W, dev, hp, launches=10,
+                                             arenas=(p, m, v, wshard))
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on one block bucket (host copies)")
         sl, sz, cs, _, _ = buckets[0]
