@@ -212,6 +212,9 @@ def zs_pack_flat(tensors: Sequence, D: int, shards: Sequence, stream=None):
         rows.append((t.data_ptr(), t.numel(), offsets[j]))
     d_table = (torch.tensor(rows, dtype=torch.int64) if rows
                else torch.zeros((0, 3), dtype=torch.int64)).to(ref.device)
+    if isinstance(stream, torch.cuda.Stream):
+        # the kernel reads the table on `stream`: tell the caching allocator
+        d_table.record_stream(stream)
     _check(load().zs_pack_flat(h, ctypes.c_void_p(d_table.data_ptr() if T else None), T, code,
                                int(D), _ptr_array(shards), S, _stream(ref, stream)))
     return d_table

@@ -93,6 +93,15 @@ struct Fd {
     }
 };
 
+// Removes a partly written file unless the save completed.
+struct TmpFile {
+    std::string path;
+    bool keep = false;
+    ~TmpFile() {
+        if (!keep && !path.empty()) ::unlink(path.c_str());
+    }
+};
+
 struct Pinned {
     void* p = nullptr;
     ~Pinned() {
@@ -251,6 +260,7 @@ ZS_EXPORT zs_status zs_shard_save(const char* path, const zs_shard_info* info, c
     Fd f;
     f.fd = ::open(tmp.c_str(), O_WRONLY | O_CREAT | O_TRUNC, 0644);
     if (f.fd < 0) return fail(ZS_EIO, "%s: cannot create %s: %s", who, tmp.c_str(), std::strerror(errno));
+    TmpFile guard{tmp};
     Pinned stage;
     hipError_t e = hipStreamSynchronize(stream);
     if (e == hipSuccess && S > 0) e = hipHostMalloc(&stage.p, size_t(kStaging), hipHostMallocDefault);
@@ -285,6 +295,7 @@ ZS_EXPORT zs_status zs_shard_save(const char* path, const zs_shard_info* info, c
     f.fd = -1;
     if (::rename(tmp.c_str(), path) != 0)
         return fail(ZS_EIO, "%s: cannot rename into %s: %s", who, path, std::strerror(errno));
+    guard.keep = true;
     return ok();
 }
 

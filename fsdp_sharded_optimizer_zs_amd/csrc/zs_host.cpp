@@ -9,12 +9,16 @@
 // denormals kept (each worker clears the SSE flush-to-zero and
 // denormals-are-zero modes for its duration), bf16 by integer
 // round-to-nearest-even. It is vectorized by the compiler (AVX2 when the CPU
-// has it, SSE2 otherwise) and split over worker threads in contiguous,
-// 64-element-aligned ranges.
+// has it, SSE2 otherwise) and split over persistent worker threads in
+// contiguous, 64-element-aligned ranges.
 
 #include <immintrin.h>
 
 #include <algorithm>
+#include <condition_variable>
+#include <cstdint>
+#include <functional>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -86,18 +90,88 @@ void run_range(float* p, float* m, float* v, uint16_t* w, const float* g, int64_
     _mm_setcsr(saved);
 }
 
+// Persistent worker threads: an offload step runs the host update once per
+// transfer chunk, and starting fresh threads for every chunk cost a few
+// milliseconds per step. Workers are created on first use, grow to the
+// largest count asked for, and serve one parallel range at a time (callers
+// from several host threads take turns).
+class Workers {
+public:
+    static Workers& get() {
+        static Workers w;
+        return w;
+    }
+
+    // Runs f(t) for t in [0, n): t = 0 on the calling thread, the rest on workers.
+    template <class F>
+    void run(int n, const F& f) {
+        std::lock_guard<std::mutex> turn(call_mu_);
+        {
+            std::unique_lock<std::mutex> lk(mu_);
+            while (int(threads_.size()) < n - 1) {
+                const int id = int(threads_.size()) + 1;
+                threads_.emplace_back([this, id] { loop(id); });
+            }
+            task_ = [&f](int t) { f(t); };
+            active_ = n;
+            remaining_ = n - 1;
+            ++generation_;
+        }
+        cv_.notify_all();
+        f(0);
+        std::unique_lock<std::mutex> lk(mu_);
+        done_cv_.wait(lk, [this] { return remaining_ == 0; });
+        task_ = nullptr;
+    }
+
+    ~Workers() {
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            stop_ = true;
+            ++generation_;
+        }
+        cv_.notify_all();
+        for (auto& t : threads_) t.join();
+    }
+
+private:
+    void loop(int id) {
+        uint64_t seen = 0;
+        for (;;) {
+            std::function<void(int)> task;
+            {
+                std::unique_lock<std::mutex> lk(mu_);
+                cv_.wait(lk, [&] { return stop_ || generation_ != seen; });
+                if (stop_) return;
+                seen = generation_;
+                if (id >= active_) continue;
+                task = task_;
+            }
+            task(id);
+            std::lock_guard<std::mutex> lk(mu_);
+            if (--remaining_ == 0) done_cv_.notify_one();
+        }
+    }
+
+    std::mutex call_mu_, mu_;
+    std::condition_variable cv_, done_cv_;
+    std::vector<std::thread> threads_;
+    std::function<void(int)> task_;
+    uint64_t generation_ = 0;
+    int active_ = 0;
+    int remaining_ = 0;
+    bool stop_ = false;
+};
+
 void parallel_step(float* p, float* m, float* v, uint16_t* w, const float* g, int64_t S,
                    const AdamConsts& k, int threads) {
     static const bool avx2 = __builtin_cpu_supports("avx2");
     const int64_t per = ((S + threads - 1) / threads + 63) / 64 * 64;
-    std::vector<std::thread> pool;
-    for (int t = 1; t < threads; ++t) {
+    const int n = int((S + per - 1) / per);
+    Workers::get().run(n, [&](int t) {
         const int64_t lo = per * t, hi = std::min(S, lo + per);
-        if (lo >= hi) break;
-        pool.emplace_back(run_range, p, m, v, w, g, lo, hi, std::cref(k), avx2);
-    }
-    run_range(p, m, v, w, g, 0, std::min(S, per), k, avx2);
-    for (auto& th : pool) th.join();
+        if (lo < hi) run_range(p, m, v, w, g, lo, hi, k, avx2);
+    });
 }
 
 zs_status check_host_state(const char* who, float* p, float* m, float* v, uint16_t* w,
