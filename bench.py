@@ -353,7 +353,7 @@ def main() -> int:
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the ZeRO-Offload (host-core AdamW) leg")
     ap.add_argument("--host-threads", type=int, default=16,
-                    help="host threads for the offload leg (the GPU box's CPU share)")
+                    help="host threads for the offload leg (default 16)")
     ap.add_argument("--no-ckpt", action="store_true",
                     help="skip the re-shard and shard checkpoint leg")
     ap.add_argument("--no-configs", action="store_true",
@@ -366,7 +366,7 @@ def main() -> int:
                     help="also run a plain 4 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+        print(f"bench.py: the shard step is measured on one GPU only (asked for --gpus {args.gpus}); the "
               "multi-GPU form of the shard step is a design, not a measured path.", file=sys.stderr)
         return 2
 
