@@ -47,8 +47,15 @@ def log(msg: str) -> None:
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the step kernels' source with comments and whitespace removed,
+    so that the stored counters stay tied to the code, not to its comments."""
+    import re
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = re.sub(r"\s+", " ", src).strip()
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def traffic_from_profiles():

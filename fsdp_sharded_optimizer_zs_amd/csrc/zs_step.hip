@@ -162,7 +162,8 @@ __device__ __forceinline__ float to_reduce_dtype(float x) {
 }
 
 // Flat reduce: g = ((c_0 + c_1) + ... + c_{n-1}) * inv_n, in rank order.
-// NC > 0 fixes n at compile time so every load is issued before the adds.
+// NC > 0 fixes n at compile time, so loads go out in batches of up to 8
+// ahead of their adds.
 template <int DT, int NC>
 struct FlatSum {
     int n;

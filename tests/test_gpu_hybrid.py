@@ -46,11 +46,12 @@ CASES = [(1, 8, False), (1, 8, True), (2, 4, False), (2, 4, True), (4, 8, True),
 
 @pytest.mark.parametrize("dtype", [O.BF16, O.FP32])
 @pytest.mark.parametrize("R,D,rnd", CASES)
-def test_reduce_ex_matches_oracle(dtype, R, D, rnd):
+@pytest.mark.parametrize("offset", [0, 1])
+def test_reduce_ex_matches_oracle(dtype, R, D, rnd, offset):
     dev = device()
     S = 3 * 2048 * 8 + 5
-    cs = contribs(R * D, S, dtype, 10 * R + D, dev)
-    out = torch.empty(S, device=dev)
+    cs = contribs(R * D, S, dtype, 10 * R + D, dev, offset)
+    out = torch.empty(S + offset, device=dev)[offset:]
     zs.zs_reduce_shard_ex(cs, out, replicas=R, round_to_reduce_dtype=rnd)
     want = O.reduce_shard_hybrid([to_np(c) for c in cs], dtype, R, rnd)
     check_f32(to_np(out), want, f"reduce R={R} D={D} rnd={rnd}", exact=True)
