@@ -395,15 +395,21 @@ def main() -> int:
     hp = dict(W.ADAMW_HP)
 
     log(f"allocating rank shard: S={S} ({S * 14 / 1e9:.1f} GB of p, m, v, w)")
-    p = torch.empty(S, device=dev)
+    # The rank's state is one arena, p | m | v | w: each fp32 array is 34.6 GB,
+    # so the three streams the step rewrites sit tens of GB apart in HBM
+    # (arrays a few GB apart run the same kernel 10-15% slower).
+    arena = torch.empty(14 * S, dtype=torch.uint8, device=dev)
+    p = arena[:4 * S].view(torch.float32)
+    m = arena[4 * S:8 * S].view(torch.float32)
+    v = arena[8 * S:12 * S].view(torch.float32)
+    wshard = arena[12 * S:].view(torch.int16)
     gen = torch.Generator(device=dev)
     gen.manual_seed(4000)
     for a in range(0, S, 1 << 30):
         b = min(S, a + (1 << 30))
         torch.randn(b - a, generator=gen, device=dev, out=p[a:b]).mul_(W.PARAM_STD)
-    m = torch.zeros(S, device=dev)
-    v = torch.zeros(S, device=dev)
-    wshard = torch.empty(S, dtype=torch.int16, device=dev)
+    m.zero_()
+    v.zero_()
     log(f"generating {CONTRIB_POOL} contribution sets of {D} x {bmax} bf16")
     pool = torch.empty((CONTRIB_POOL, D, bmax), dtype=torch.int16, device=dev)
     for s in range(CONTRIB_POOL):
