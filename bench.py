@@ -533,6 +533,10 @@ def main() -> int:
     bpp = 26 + D * es                              # fused: 12 read + 14 written + D*es
     adam_launches = K * n_launch
     adam_avg_s = adam_ms / 1e3 / adam_launches
+    # median per-launch rate over the timed launches
+    bucket_rates = sorted(bpp * sz / (e[0].elapsed_time(e[1]) / 1e3) / 1e9
+                          for evs in ev for e, (_, sz, _, _, _) in zip(evs, buckets))
+    median_rate = bucket_rates[len(bucket_rates) // 2]
     bytes_per_launch = bpp * S / n_launch
     achieved = bytes_per_launch / adam_avg_s / 1e9
     gather_bytes = 4.0 * D * S                     # D*S bf16 read + written per step
@@ -573,6 +577,7 @@ def main() -> int:
             "algorithmic_bytes_per_param": bpp,
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "avg_launch_ms": adam_avg_s * 1e3,
+            "median_launch_GB_s": median_rate,
             "stream_ceiling": ceiling,
         },
         "adamw_fused": {"params_per_s": S * K / (adam_ms / 1e3),
@@ -622,10 +627,18 @@ def main() -> int:
         sl, sz, cs, _, _ = buckets[0]
         # one step of the oracle from the bucket's current state
         rate, secs, n = cpu_baseline(p[sl], m[sl], v[sl], cs, args.warmup + K + 2, hp)
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+        except OSError:
+            pass
         out["cpu_baseline"] = {
             "value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"one block bucket of the same workload ({n} params, D=8 bf16 "
                       f"contributions), one step, {secs:.1f} s of single-threaded numpy",
+            "host": {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+                     "cpu_model": model},
         }
     print(json.dumps(out), flush=True)
     return 0
