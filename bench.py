@@ -154,21 +154,25 @@ def pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D, step_t, hp, host_
     return res
 
 
-def hybrid_leg(zs, torch, W, dev, hp, steps: int):
+def hybrid_leg(zs, torch, W, dev, hp, steps: int, arenas):
     """HYBRID_SHARD shard step on the full LLaMA-7B rank shard of a 4-node x
     8-GPU job (D = 8 per node, 4 replica groups, bf16 collectives): one
     zs_adamw_step_ex per unit bucket (33), 32 bf16 contributions each. The
     same buckets are also stepped with the flat 32-contribution reduce
-    (zs_adamw_step), which moves the same 26 + 32 * 2 = 90 B/param."""
+    (zs_adamw_step), which moves the same 26 + 32 * 2 = 90 B/param. The
+    shard's p, m, v and w are placed at the start of the 70B run's state
+    arrays (`arenas`, re-initialized here), tens of GB apart as a rank's own
+    state arrays are."""
     w = W.get("llama7b_hybrid")
     R, D = w.replicas, w.D
     sizes = [zs.zs_unit_layout(u.numels, D)[3] for u in w.units]
     S = int(sum(sizes))
     bmax = max(sizes)
-    p = W.master_init(S, 6000, dev)
-    m = torch.zeros(S, device=dev)
-    v = torch.zeros(S, device=dev)
-    ws = torch.empty(S, dtype=torch.int16, device=dev)
+    P, M, V, WS = arenas
+    p, m, v, ws = P[:S], M[:S], V[:S], WS[:S]
+    p.copy_(W.master_init(S, 6000, dev))
+    m.zero_()
+    v.zero_()
     pool = torch.empty((2, R * D, bmax), dtype=torch.int16, device=dev)
     for s_ in range(2):
         for k in range(R * D):
@@ -203,7 +207,7 @@ def hybrid_leg(zs, torch, W, dev, hp, steps: int):
         ms = e0.elapsed_time(e1) / steps
         res[name] = {"ms_per_step": ms, "params_per_s": S / (ms / 1e3),
                      "GB_s": (26 + R * D * 2) * S / (ms / 1e3) / 1e9}
-    del p, m, v, ws, pool
+    del pool
     torch.cuda.empty_cache()
     return res
 
@@ -617,7 +621,8 @@ def main() -> int:
         out["offload"] = offload_leg(zs, torch, W, dev, hp, args.host_threads)
     if not args.no_hybrid:
         log("hybrid leg: LLaMA-7B rank shard under HYBRID_SHARD, 4 x 8 contributions")
-        out["hybrid_shard"] = hybrid_leg(zs, torch, W, dev, hp, steps=3)
+        out["hybrid_shard"] = hybrid_leg(zs, torch, W, dev, hp, steps=3,
+                                         arenas=(p, m, v, wshard))
     if not args.no_configs:
         log("configs leg: the fused kernel on the other workloads' rank shards")
         out["other_workloads"] = configs_leg(zs, torch, W, dev, hp, launches=10,

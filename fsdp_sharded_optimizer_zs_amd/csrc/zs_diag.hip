@@ -4,11 +4,17 @@
 // written: 2 reads per write at n = 8 bf16), not only against the datasheet
 // peak.
 //
-// Same launch shape, lane map, vector widths and cache hints as the fused
-// kernel: 8 elements per lane, non-temporal contribution loads, temporal
-// state loads, non-temporal stores, a persistent grid of the same size. The
-// values written are placeholders (p + m, v, p and an XOR of the
-// contributions); the buffers' contents are not meaningful afterwards.
+// Same launch shape, occupancy, tiles, lane maps, vector widths and cache
+// hints as the fused kernel: two adjacent 512-element tiles per wavefront and
+// iteration (whole pairs only);
+// bf16 contributions in the run map (lane t: elements 8t..8t+7), their
+// combined value moved to the split map (lane t: 4t..4t+3 and
+// 256+4t..256+4t+3) through LDS; fp32 contributions and p, m, v in the split
+// map; non-temporal contribution loads, temporal state loads, non-temporal
+// stores, a persistent grid of the same size. The values written are
+// placeholders: p + m into p, v into m, p into v, and into w the first two
+// words of each 16-byte XOR of the contributions (bf16: taken after the LDS
+// exchange, the odd entries with 1 XORed into every word).
 
 #include "zs_internal.h"
 
@@ -17,57 +23,110 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
+constexpr int kWave = 64;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kTile = 512;
+constexpr int kPair = ZS_STEP_TILES;
 
-// VW: 16-byte vectors of one contribution per 8 elements (1 for bf16, 2 for fp32)
-template <int VW>
-__global__ __launch_bounds__(kThreads) void streams_kernel(float* __restrict__ p,
-                                                           float* __restrict__ m,
-                                                           float* __restrict__ v,
-                                                           uint16_t* __restrict__ w, int64_t nvec,
-                                                           PtrPack c, int n) {
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The streams of TP adjacent tiles from tile0: state loads first, then the
+// contributions, then the stores, as in the fused kernel. BF16: contributions
+// are one run-map 16-byte vector per lane; otherwise two split-map vectors.
+template <bool BF16, int TP>
+__device__ __forceinline__ void tiles(f32x4* __restrict__ p4, f32x4* __restrict__ m4,
+                                      f32x4* __restrict__ v4, u32x2* __restrict__ w2,
+                                      const PtrPack& c, int n, int64_t tile0, int lane,
+                                      u32x4* slot) {
+    f32x4 pa[TP], pb[TP], ma[TP], mb[TP], va[TP], vb[TP];
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+        const int64_t a = (tile0 + u) * (kTile / 4) + lane, b = a + kWave;
+        pa[u] = p4[a], pb[u] = p4[b];
+        ma[u] = m4[a], mb[u] = m4[b];
+        va[u] = v4[a], vb[u] = v4[b];
+    }
+    u32x4 sa[TP], sb[TP];
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+        sa[u] = u32x4{0u, 0u, 0u, 0u};
+        sb[u] = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (BF16) {
+#pragma unroll 8
+            for (int q = 0; q < n; ++q)
+                sa[u] ^= __builtin_nontemporal_load(static_cast<const u32x4*>(c.p[q]) +
+                                                    (tile0 + u) * kWave + lane);
+        } else {
+#pragma unroll 8
+            for (int q = 0; q < n; ++q) {
+                const u32x4* cq =
+                    static_cast<const u32x4*>(c.p[q]) + (tile0 + u) * (kTile / 4) + lane;
+                sa[u] ^= __builtin_nontemporal_load(cq);
+                sb[u] ^= __builtin_nontemporal_load(cq + kWave);
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+        if constexpr (BF16) {
+            // the fused kernel moves 8 fp32 values (two 16-byte entries) per lane
+            slot[2 * lane] = sa[u];
+            slot[2 * lane + 1] = sa[u] ^ u32x4{1u, 1u, 1u, 1u};
+            wave_sync();
+            sa[u] = slot[lane];
+            sb[u] = slot[kWave + lane];
+            wave_sync();
+        }
+        const int64_t a = (tile0 + u) * (kTile / 4) + lane, b = a + kWave;
+        __builtin_nontemporal_store(pa[u] + ma[u], p4 + a);
+        __builtin_nontemporal_store(pb[u] + mb[u], p4 + b);
+        __builtin_nontemporal_store(va[u], m4 + a);
+        __builtin_nontemporal_store(vb[u], m4 + b);
+        __builtin_nontemporal_store(pa[u], v4 + a);
+        __builtin_nontemporal_store(pb[u], v4 + b);
+        __builtin_nontemporal_store(u32x2{sa[u].x, sa[u].y}, w2 + a);
+        __builtin_nontemporal_store(u32x2{sb[u].x, sb[u].y}, w2 + b);
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void
+streams_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
+               uint16_t* __restrict__ w, int64_t npairs, PtrPack c, int n) {
+    __shared__ u32x4 xpose[kWaves][kTile / 4];
+    const int lane = int(threadIdx.x) % kWave;
+    const int wave = int(threadIdx.x) / kWave;
     f32x4* p4 = reinterpret_cast<f32x4*>(p);
     f32x4* m4 = reinterpret_cast<f32x4*>(m);
     f32x4* v4 = reinterpret_cast<f32x4*>(v);
-    u32x4* w4 = reinterpret_cast<u32x4*>(w);
-    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec;
-         i += int64_t(gridDim.x) * kThreads) {
-        u32x4 s = {0u, 0u, 0u, 0u};
-#pragma unroll 8
-        for (int q = 0; q < n; ++q) {
-            const u32x4* cq = static_cast<const u32x4*>(c.p[q]) + VW * i;
-#pragma unroll
-            for (int h = 0; h < VW; ++h) s ^= __builtin_nontemporal_load(cq + h);
-        }
-        const f32x4 pa = p4[2 * i], pb = p4[2 * i + 1];
-        const f32x4 ma = m4[2 * i], mb = m4[2 * i + 1];
-        const f32x4 va = v4[2 * i], vb = v4[2 * i + 1];
-        __builtin_nontemporal_store(pa + ma, p4 + 2 * i);
-        __builtin_nontemporal_store(pb + mb, p4 + 2 * i + 1);
-        __builtin_nontemporal_store(va, m4 + 2 * i);
-        __builtin_nontemporal_store(vb, m4 + 2 * i + 1);
-        __builtin_nontemporal_store(pa, v4 + 2 * i);
-        __builtin_nontemporal_store(pb, v4 + 2 * i + 1);
-        __builtin_nontemporal_store(s, w4 + i);
-    }
+    u32x2* w2 = reinterpret_cast<u32x2*>(w);
+    for (int64_t q = int64_t(blockIdx.x) * kWaves + wave; q < npairs;
+         q += int64_t(gridDim.x) * kWaves)
+        tiles<BF16, kPair>(p4, m4, v4, w2, c, n, q * kPair, lane, xpose[wave]);
 }
 
 }  // namespace
 
 hipError_t launch_streams(float* p, float* m, float* v, uint16_t* w, int64_t S,
                           const PtrPack& contribs, int n, int dtype, hipStream_t stream) {
-    const int64_t nvec = S / 8;
+    const int64_t npairs = S / (kPair * kTile);
     const int64_t cap = int64_t(device_info().cu_count) * ZS_STEP_BLOCKS_PER_CU;
-    int64_t blocks = (nvec + kThreads - 1) / kThreads;
+    int64_t blocks = (npairs + kWaves - 1) / kWaves;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     if (dtype == ZS_BF16)
-        hipLaunchKernelGGL((streams_kernel<1>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                           p, m, v, w, nvec, contribs, n);
+        hipLaunchKernelGGL((streams_kernel<true>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+                           stream, p, m, v, w, npairs, contribs, n);
     else
-        hipLaunchKernelGGL((streams_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                           p, m, v, w, nvec, contribs, n);
+        hipLaunchKernelGGL((streams_kernel<false>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+                           stream, p, m, v, w, npairs, contribs, n);
     return hipGetLastError();
 }
 

@@ -7,12 +7,19 @@
 
 #include "../../include/zs.h"
 
-// Workgroups of 256 threads per CU for the step kernels' persistent grid:
-// 2 per CU (8 wavefronts) was the fastest setting measured on MI355X over
-// the 81 buckets of a 70B rank shard; 1, 4 and 8 per CU, 4-element lanes
-// and 512-element wave tiles were all equal or slower.
+// Launch shape of the tiled step kernels (workgroups of 256 threads): tiles
+// per wavefront and iteration, and workgroups per CU for the persistent grid.
+// Two adjacent 512-element tiles per iteration with one workgroup per CU was
+// the fastest shape measured on MI355X: over the 81 buckets of a 70B rank
+// shard 6.05-6.11 TB/s, against 5.94-6.04 with single tiles and two
+// workgroups per CU, 5.74 with three tiles; equal or better too for 32- and
+// 16-contribution folds (the full LLaMA-7B shard at D = 32, the ragged fp32
+// unit at D = 16, the HYBRID_SHARD buckets).
+#ifndef ZS_STEP_TILES
+#define ZS_STEP_TILES 2
+#endif
 #ifndef ZS_STEP_BLOCKS_PER_CU
-#define ZS_STEP_BLOCKS_PER_CU 2
+#define ZS_STEP_BLOCKS_PER_CU 1
 #endif
 
 namespace zs {

@@ -4,10 +4,26 @@
 // Both kernels are streaming, elementwise and HBM-bound: per element they
 // read the D gradient contributions (and p, m, v), do a few dozen VALU
 // operations and write the results once. There is no dense contraction, so
-// no MFMA and no LDS: every lane owns 8 consecutive elements, moved with
-// 16-byte (dwordx4) loads and stores, and a persistent grid sized to the CU
-// count walks the shard in grid-stride order, so each wavefront's accesses
-// are fully coalesced 1 KiB runs per stream.
+// no MFMA. Work goes in 512-element tiles, 8 elements per lane; a wavefront
+// takes two adjacent tiles per iteration, and a persistent grid of one
+// workgroup per CU walks the tile pairs in grid-stride order. Inside a tile
+// two lane maps are used:
+//
+//   run map:   lane t holds elements 8t .. 8t+7 (one 16-byte bf16 vector);
+//   split map: lane t holds elements 4t .. 4t+3 and 256+4t .. 256+4t+3 (two
+//              16-byte fp32 vectors).
+//
+// Every load and store instruction of a wavefront then covers one contiguous
+// run of whole cache lines: bf16 contributions load in the run map (1 KiB),
+// fp32 contributions and the state p, m, v load and store in the split map
+// (1 KiB), and the bf16 working shard leaves in the split map as two 512-byte
+// stores. The fp32 sums of bf16 contributions are moved from the run map to
+// the split map through a 2 KiB LDS slot per wavefront. (With the run map for
+// fp32 too, a lane's 32 bytes went out as two 16-byte stores and lines could
+// leave L2 half written: 3.6% more HBM writes. On MI355X's 70B buckets the
+// split map with tile pairs and one workgroup per CU runs the step at
+// 6.05-6.11 TB/s, against 5.94-6.04 for the run map with two workgroups per
+// CU.)
 //
 // The arithmetic follows the operation order fixed for the step exactly:
 // contributions widened exactly and folded left to right in rank order,
@@ -24,7 +40,7 @@
 // read-once contributions and non-temporal stores; the state p, m, v is
 // loaded with temporal loads, because non-temporal loads of lines that the
 // same lane then rewrites measured 20% slower (4.9 against 6.0 TB/s). The
-// launch shape (ZS_STEP_BLOCKS_PER_CU) is in zs_internal.h.
+// launch shape (ZS_STEP_TILES, ZS_STEP_BLOCKS_PER_CU) is in zs_internal.h.
 #ifndef ZS_NT_LOADS
 #define ZS_NT_LOADS 1
 #endif
@@ -37,9 +53,23 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;  // 4 wavefronts of 64
-constexpr int kVec = 8;        // elements per lane per iteration
+constexpr int kThreads = 256;               // 4 wavefronts of 64
+constexpr int kWave = 64;
+constexpr int kWaves = kThreads / kWave;    // wavefronts per workgroup
+constexpr int kVec = 8;                     // elements per lane per tile
+constexpr int kTile = kWave * kVec;         // elements per wavefront tile
+
+// Occupancy the tiled kernels are compiled for: at most 2 wavefronts per
+// SIMD, so up to 256 VGPRs each and the scheduler issues a tile pair's 28
+// loads before their first use. Without it the compiler spends registers for
+// an occupancy the persistent grid never uses and serializes the loads
+// (3.5-5.9 TB/s on MI355X); at most 1 wavefront per SIMD keeps a second
+// workgroup off any CU, and the grid's last workgroups then wait (3.6 TB/s).
+#ifndef ZS_WAVES
+#define ZS_WAVES __attribute__((amdgpu_waves_per_eu(1, 2)))
+#endif
 
 // Streamed (read-once) loads and write-once stores.
 template <typename T>
@@ -73,20 +103,22 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
     return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rounded;
 }
 
-// Contribution q's 8 elements at vector index i, widened to fp32.
+// One contribution's 8 elements for lane `lane` of tile `tile`, widened to
+// fp32: bf16 in the run map, fp32 in the split map.
 template <int DT>
-__device__ __forceinline__ void load8(const void* base, int64_t i, float (&x)[kVec]) {
+__device__ __forceinline__ void load8(const void* base, int64_t tile, int lane,
+                                      float (&x)[kVec]) {
     if constexpr (DT == ZS_BF16) {
-        const u32x4 h = ld_once(static_cast<const u32x4*>(base) + i);
+        const u32x4 h = ld_once(static_cast<const u32x4*>(base) + tile * kWave + lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             x[2 * e] = bf16_lo(h[e]);
             x[2 * e + 1] = bf16_hi(h[e]);
         }
     } else {
-        const f32x4* b = static_cast<const f32x4*>(base) + 2 * i;
+        const f32x4* b = static_cast<const f32x4*>(base) + tile * (kTile / 4) + lane;
         const f32x4 a0 = ld_once(b);
-        const f32x4 a1 = ld_once(b + 1);
+        const f32x4 a1 = ld_once(b + kWave);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             x[e] = a0[e];
@@ -113,11 +145,11 @@ __device__ __forceinline__ float load1(const void* base, int64_t i) {
 constexpr int kBatch = 8;
 
 template <int DT, int NB>
-__device__ __forceinline__ void add_batch(const PtrPack& c, int first, int64_t i,
+__device__ __forceinline__ void add_batch(const PtrPack& c, int first, int64_t tile, int lane,
                                           float (&s)[kVec]) {
     float x[NB][kVec];
 #pragma unroll
-    for (int q = 0; q < NB; ++q) load8<DT>(c.p[first + q], i, x[q]);
+    for (int q = 0; q < NB; ++q) load8<DT>(c.p[first + q], tile, lane, x[q]);
 #pragma unroll
     for (int q = 0; q < NB; ++q)
 #pragma unroll
@@ -125,25 +157,25 @@ __device__ __forceinline__ void add_batch(const PtrPack& c, int first, int64_t i
 }
 
 template <int DT, int NC>
-__device__ __forceinline__ void fold8(const PtrPack& c, int base, int n, int64_t i,
+__device__ __forceinline__ void fold8(const PtrPack& c, int base, int n, int64_t tile, int lane,
                                       float (&s)[kVec]) {
     if constexpr (NC > 0 && NC <= kBatch) {
-        load8<DT>(c.p[base], i, s);
-        if constexpr (NC > 1) add_batch<DT, NC - 1>(c, base + 1, i, s);
+        load8<DT>(c.p[base], tile, lane, s);
+        if constexpr (NC > 1) add_batch<DT, NC - 1>(c, base + 1, tile, lane, s);
     } else {
         const int len = NC > 0 ? NC : n;
         // first batch: c_0 then up to 7 more
         const int head = len < kBatch ? len : kBatch;
-        load8<DT>(c.p[base], i, s);
+        load8<DT>(c.p[base], tile, lane, s);
         int q = 1;
         if (head == kBatch) {
-            add_batch<DT, kBatch - 1>(c, base + 1, i, s);
+            add_batch<DT, kBatch - 1>(c, base + 1, tile, lane, s);
             q = kBatch;
         }
 #pragma unroll 1
-        for (; q + kBatch <= len; q += kBatch) add_batch<DT, kBatch>(c, base + q, i, s);
+        for (; q + kBatch <= len; q += kBatch) add_batch<DT, kBatch>(c, base + q, tile, lane, s);
 #pragma unroll 1
-        for (; q < len; ++q) add_batch<DT, 1>(c, base + q, i, s);
+        for (; q < len; ++q) add_batch<DT, 1>(c, base + q, tile, lane, s);
     }
 }
 
@@ -168,8 +200,9 @@ template <int DT, int NC>
 struct FlatSum {
     int n;
     float inv_n;
-    __device__ __forceinline__ void vec(const PtrPack& c, int64_t i, float (&g)[kVec]) const {
-        fold8<DT, NC>(c, 0, n, i, g);
+    __device__ __forceinline__ void vec(const PtrPack& c, int64_t tile, int lane,
+                                        float (&g)[kVec]) const {
+        fold8<DT, NC>(c, 0, n, tile, lane, g);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) g[e] = g[e] * inv_n;
     }
@@ -188,15 +221,16 @@ struct HybridSum {
     int R;
     int rnd;
     float inv_n;
-    __device__ __forceinline__ void vec(const PtrPack& c, int64_t i, float (&g)[kVec]) const {
-        fold8<DT, NC>(c, 0, nd, i, g);
+    __device__ __forceinline__ void vec(const PtrPack& c, int64_t tile, int lane,
+                                        float (&g)[kVec]) const {
+        fold8<DT, NC>(c, 0, nd, tile, lane, g);
         if (rnd) {
 #pragma unroll
             for (int e = 0; e < kVec; ++e) g[e] = to_reduce_dtype<DT>(g[e]);
         }
         for (int j = 1; j < R; ++j) {
             float s[kVec];
-            fold8<DT, NC>(c, j * nd, nd, i, s);
+            fold8<DT, NC>(c, j * nd, nd, tile, lane, s);
 #pragma unroll
             for (int e = 0; e < kVec; ++e) g[e] = g[e] + (rnd ? to_reduce_dtype<DT>(s[e]) : s[e]);
         }
@@ -228,53 +262,115 @@ __device__ __forceinline__ void adamw1(float& p, float& m, float& v, float g,
 
 // ---------------------------------------------------------------- kernels
 
-// Fused reduce + AdamW over 8-element vectors; 16-byte aligned buffers.
-// The last block also handles the S % 8 tail elements one per lane.
-template <int DT, class Sum>
-__global__ __launch_bounds__(kThreads) void adamw_vec_kernel(
-    float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
-    uint16_t* __restrict__ w, int64_t S, PtrPack c, Sum sum, AdamConsts k) {
-    const int64_t nvec = S / kVec;
-    const int64_t stride = int64_t(gridDim.x) * kThreads;
-    f32x4* p4 = reinterpret_cast<f32x4*>(p);
-    f32x4* m4 = reinterpret_cast<f32x4*>(m);
-    f32x4* v4 = reinterpret_cast<f32x4*>(v);
-    u32x4* w4 = reinterpret_cast<u32x4*>(w);
-    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride) {
-        float g[kVec];
-        sum.vec(c, i, g);
-        const f32x4 pa = p4[2 * i], pb = p4[2 * i + 1];
-        const f32x4 ma = m4[2 * i], mb = m4[2 * i + 1];
-        const f32x4 va = v4[2 * i], vb = v4[2 * i + 1];
+// Order the wavefront's LDS accesses before and after this point (the LDS
+// serves one wavefront's instructions in issue order).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The 8 values of a lane from the run map to the split map, through the
+// wavefront's slot of 128 16-byte entries (entry k: tile elements 4k..4k+3).
+__device__ __forceinline__ void run_to_split(float (&g)[kVec], f32x4* slot, int lane) {
+    slot[2 * lane] = f32x4{g[0], g[1], g[2], g[3]};
+    slot[2 * lane + 1] = f32x4{g[4], g[5], g[6], g[7]};
+    wave_sync();
+    const f32x4 a = slot[lane];
+    const f32x4 b = slot[kWave + lane];
+    wave_sync();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        g[e] = a[e];
+        g[4 + e] = b[e];
+    }
+}
+
+// AdamW on TP adjacent tiles from tile0, lane `lane`: all state loads, then
+// the contributions of every tile, then the arithmetic and the stores.
+template <int DT, int TP, class Sum>
+__device__ __forceinline__ void adamw_tiles(f32x4* __restrict__ p4, f32x4* __restrict__ m4,
+                                            f32x4* __restrict__ v4, u32x2* __restrict__ w2,
+                                            const PtrPack& c, const Sum& sum, const AdamConsts& k,
+                                            int64_t tile0, int lane, f32x4* slot) {
+    f32x4 pa[TP], pb[TP], ma[TP], mb[TP], va[TP], vb[TP];
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+        const int64_t a = (tile0 + u) * (kTile / 4) + lane;  // split map: elements 4a .. 4a+3
+        const int64_t b = a + kWave;                          // and 4b .. 4b+3 (256 further)
+        pa[u] = p4[a], pb[u] = p4[b];
+        ma[u] = m4[a], mb[u] = m4[b];
+        va[u] = v4[a], vb[u] = v4[b];
+    }
+    float g[TP][kVec];
+#pragma unroll
+    for (int u = 0; u < TP; ++u) sum.vec(c, tile0 + u, lane, g[u]);
+    // every tile's exchange (an LDS round trip between wavefront fences) before
+    // any tile's arithmetic, so that no fence sits between one tile's stores
+    // and the next tile's use of its loads
+    if constexpr (DT == ZS_BF16) {
+#pragma unroll
+        for (int u = 0; u < TP; ++u) run_to_split(g[u], slot, lane);
+    }
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+        const int64_t a = (tile0 + u) * (kTile / 4) + lane;
+        const int64_t b = a + kWave;
         float pp[kVec], mm[kVec], vv[kVec];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            pp[e] = pa[e], pp[4 + e] = pb[e];
-            mm[e] = ma[e], mm[4 + e] = mb[e];
-            vv[e] = va[e], vv[4 + e] = vb[e];
+            pp[e] = pa[u][e], pp[4 + e] = pb[u][e];
+            mm[e] = ma[u][e], mm[4 + e] = mb[u][e];
+            vv[e] = va[u][e], vv[4 + e] = vb[u][e];
         }
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) adamw1(pp[e], mm[e], vv[e], g[e], k);
-        u32x4 wv;
+        for (int e = 0; e < kVec; ++e) adamw1(pp[e], mm[e], vv[e], g[u][e], k);
+        u32x2 wa, wb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wv[e] = f32_to_bf16(pp[2 * e]) | (f32_to_bf16(pp[2 * e + 1]) << 16);
-        st_once(f32x4{pp[0], pp[1], pp[2], pp[3]}, p4 + 2 * i);
-        st_once(f32x4{pp[4], pp[5], pp[6], pp[7]}, p4 + 2 * i + 1);
-        st_once(f32x4{mm[0], mm[1], mm[2], mm[3]}, m4 + 2 * i);
-        st_once(f32x4{mm[4], mm[5], mm[6], mm[7]}, m4 + 2 * i + 1);
-        st_once(f32x4{vv[0], vv[1], vv[2], vv[3]}, v4 + 2 * i);
-        st_once(f32x4{vv[4], vv[5], vv[6], vv[7]}, v4 + 2 * i + 1);
-        st_once(wv, w4 + i);
+        for (int e = 0; e < 2; ++e) {
+            wa[e] = f32_to_bf16(pp[2 * e]) | (f32_to_bf16(pp[2 * e + 1]) << 16);
+            wb[e] = f32_to_bf16(pp[4 + 2 * e]) | (f32_to_bf16(pp[5 + 2 * e]) << 16);
+        }
+        st_once(f32x4{pp[0], pp[1], pp[2], pp[3]}, p4 + a);
+        st_once(f32x4{pp[4], pp[5], pp[6], pp[7]}, p4 + b);
+        st_once(f32x4{mm[0], mm[1], mm[2], mm[3]}, m4 + a);
+        st_once(f32x4{mm[4], mm[5], mm[6], mm[7]}, m4 + b);
+        st_once(f32x4{vv[0], vv[1], vv[2], vv[3]}, v4 + a);
+        st_once(f32x4{vv[4], vv[5], vv[6], vv[7]}, v4 + b);
+        st_once(wa, w2 + a);
+        st_once(wb, w2 + b);
     }
-    const int64_t t = nvec * kVec + threadIdx.x;
-    if (blockIdx.x == gridDim.x - 1 && t < S) {
-        const float g = sum.one(c, t);
-        float pp = p[t], mm = m[t], vv = v[t];
-        adamw1(pp, mm, vv, g, k);
-        p[t] = pp;
-        m[t] = mm;
-        v[t] = vv;
-        w[t] = uint16_t(f32_to_bf16(pp));
+}
+
+// Fused reduce + AdamW over whole groups of TP adjacent 512-element tiles,
+// one group per wavefront and iteration; 16-byte aligned buffers. The last
+// workgroup also takes the elements past the last whole group (fewer than
+// TP * 512), one per lane.
+template <int DT, class Sum, int TP>
+__global__ __launch_bounds__(kThreads) ZS_WAVES void adamw_vec_kernel(
+    float* __restrict__ p, float* __restrict__ m, float* __restrict__ v,
+    uint16_t* __restrict__ w, int64_t S, PtrPack c, Sum sum, AdamConsts k) {
+    __shared__ f32x4 xpose[kWaves][kTile / 4];
+    const int lane = int(threadIdx.x) % kWave;
+    const int wave = int(threadIdx.x) / kWave;
+    const int64_t stride = int64_t(gridDim.x) * kWaves;
+    f32x4* p4 = reinterpret_cast<f32x4*>(p);
+    f32x4* m4 = reinterpret_cast<f32x4*>(m);
+    f32x4* v4 = reinterpret_cast<f32x4*>(v);
+    u32x2* w2 = reinterpret_cast<u32x2*>(w);
+    const int64_t ngroups = S / (TP * kTile);
+    for (int64_t q = int64_t(blockIdx.x) * kWaves + wave; q < ngroups; q += stride)
+        adamw_tiles<DT, TP>(p4, m4, v4, w2, c, sum, k, q * TP, lane, xpose[wave]);
+    if (blockIdx.x == gridDim.x - 1) {
+        for (int64_t t = ngroups * TP * kTile + threadIdx.x; t < S; t += kThreads) {
+            const float g = sum.one(c, t);
+            float pp = p[t], mm = m[t], vv = v[t];
+            adamw1(pp, mm, vv, g, k);
+            p[t] = pp;
+            m[t] = mm;
+            v[t] = vv;
+            w[t] = uint16_t(f32_to_bf16(pp));
+        }
     }
 }
 
@@ -295,21 +391,43 @@ __global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(
     }
 }
 
-// Unfused reduce: g written to HBM (fp32).
-template <int DT, class Sum>
-__global__ __launch_bounds__(kThreads) void reduce_vec_kernel(float* __restrict__ out, int64_t S,
-                                                              PtrPack c, Sum sum) {
-    const int64_t nvec = S / kVec;
-    const int64_t stride = int64_t(gridDim.x) * kThreads;
-    f32x4* o4 = reinterpret_cast<f32x4*>(out);
-    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride) {
-        float g[kVec];
-        sum.vec(c, i, g);
-        st_once(f32x4{g[0], g[1], g[2], g[3]}, o4 + 2 * i);
-        st_once(f32x4{g[4], g[5], g[6], g[7]}, o4 + 2 * i + 1);
+// The reduced gradient of TP adjacent tiles from tile0, stored in the split map.
+template <int DT, int TP, class Sum>
+__device__ __forceinline__ void reduce_tiles(f32x4* __restrict__ o4, const PtrPack& c,
+                                             const Sum& sum, int64_t tile0, int lane,
+                                             f32x4* slot) {
+    float g[TP][kVec];
+#pragma unroll
+    for (int u = 0; u < TP; ++u) sum.vec(c, tile0 + u, lane, g[u]);
+    if constexpr (DT == ZS_BF16) {
+#pragma unroll
+        for (int u = 0; u < TP; ++u) run_to_split(g[u], slot, lane);
     }
-    const int64_t t = nvec * kVec + threadIdx.x;
-    if (blockIdx.x == gridDim.x - 1 && t < S) out[t] = sum.one(c, t);
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+        const int64_t a = (tile0 + u) * (kTile / 4) + lane;
+        st_once(f32x4{g[u][0], g[u][1], g[u][2], g[u][3]}, o4 + a);
+        st_once(f32x4{g[u][4], g[u][5], g[u][6], g[u][7]}, o4 + a + kWave);
+    }
+}
+
+// Unfused reduce: g written to HBM (fp32), tiles as in adamw_vec_kernel.
+template <int DT, class Sum, int TP>
+__global__ __launch_bounds__(kThreads) ZS_WAVES void reduce_vec_kernel(float* __restrict__ out,
+                                                                       int64_t S, PtrPack c,
+                                                                       Sum sum) {
+    __shared__ f32x4 xpose[kWaves][kTile / 4];
+    const int lane = int(threadIdx.x) % kWave;
+    const int wave = int(threadIdx.x) / kWave;
+    const int64_t stride = int64_t(gridDim.x) * kWaves;
+    f32x4* o4 = reinterpret_cast<f32x4*>(out);
+    const int64_t ngroups = S / (TP * kTile);
+    for (int64_t q = int64_t(blockIdx.x) * kWaves + wave; q < ngroups; q += stride)
+        reduce_tiles<DT, TP>(o4, c, sum, q * TP, lane, xpose[wave]);
+    if (blockIdx.x == gridDim.x - 1) {
+        for (int64_t t = ngroups * TP * kTile + threadIdx.x; t < S; t += kThreads)
+            out[t] = sum.one(c, t);
+    }
 }
 
 template <int DT, class Sum>
@@ -322,12 +440,16 @@ __global__ __launch_bounds__(kThreads) void reduce_scalar_kernel(float* __restri
 
 // ---------------------------------------------------------------- dispatch
 
-int grid_for(int64_t work_items) {
-    const int64_t cap = int64_t(device_info().cu_count) * ZS_STEP_BLOCKS_PER_CU;
-    int64_t blocks = (work_items + kThreads - 1) / kThreads;
+// Workgroups for `lanes` lanes of work (elements for the scalar kernels,
+// tile groups x 64 for the tiled ones), capped at `per_cu` per CU.
+int grid_for(int64_t lanes, int per_cu) {
+    const int64_t cap = int64_t(device_info().cu_count) * per_cu;
+    int64_t blocks = (lanes + kThreads - 1) / kThreads;
     if (blocks > cap) blocks = cap;
     return blocks < 1 ? 1 : int(blocks);
 }
+
+constexpr int kScalarBlocksPerCu = 2;  // the element-at-a-time fallback kernels
 
 // What one launch computes: the AdamW step (out == nullptr) or the reduce
 // alone into out.
@@ -344,20 +466,23 @@ struct Job {
 
 template <int DT, class Sum>
 hipError_t launch_job(const Job& j, const PtrPack& c, const Sum& sum, hipStream_t stream) {
+    constexpr int TP = ZS_STEP_TILES;
+    const int tiled = grid_for(j.S / (TP * kTile) * kWave, ZS_STEP_BLOCKS_PER_CU);
+    const int scalar = grid_for(j.S, kScalarBlocksPerCu);
     if (j.out == nullptr) {
         if (j.aligned)
-            hipLaunchKernelGGL((adamw_vec_kernel<DT, Sum>), dim3(grid_for(j.S / kVec)),
-                               dim3(kThreads), 0, stream, j.p, j.m, j.v, j.w, j.S, c, sum, j.k);
+            hipLaunchKernelGGL((adamw_vec_kernel<DT, Sum, TP>), dim3(tiled), dim3(kThreads), 0,
+                               stream, j.p, j.m, j.v, j.w, j.S, c, sum, j.k);
         else
-            hipLaunchKernelGGL((adamw_scalar_kernel<DT, Sum>), dim3(grid_for(j.S)), dim3(kThreads),
-                               0, stream, j.p, j.m, j.v, j.w, j.S, c, sum, j.k);
+            hipLaunchKernelGGL((adamw_scalar_kernel<DT, Sum>), dim3(scalar), dim3(kThreads), 0,
+                               stream, j.p, j.m, j.v, j.w, j.S, c, sum, j.k);
     } else {
         if (j.aligned)
-            hipLaunchKernelGGL((reduce_vec_kernel<DT, Sum>), dim3(grid_for(j.S / kVec)),
-                               dim3(kThreads), 0, stream, j.out, j.S, c, sum);
+            hipLaunchKernelGGL((reduce_vec_kernel<DT, Sum, TP>), dim3(tiled), dim3(kThreads), 0,
+                               stream, j.out, j.S, c, sum);
         else
-            hipLaunchKernelGGL((reduce_scalar_kernel<DT, Sum>), dim3(grid_for(j.S)),
-                               dim3(kThreads), 0, stream, j.out, j.S, c, sum);
+            hipLaunchKernelGGL((reduce_scalar_kernel<DT, Sum>), dim3(scalar), dim3(kThreads), 0,
+                               stream, j.out, j.S, c, sum);
     }
     return hipGetLastError();
 }

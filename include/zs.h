@@ -450,7 +450,7 @@ zs_status zs_offload_step(const void* const* contribs, int32_t D, int32_t dtype,
  * launch shape, lane map and cache hints, so that the step kernel can be
  * read against what HBM delivers for its own mix of streams. The values it
  * writes are placeholders: p, m, v and w are garbage afterwards. Processes
- * the first 8 * floor(S / 8) elements; every buffer 16-byte aligned.
+ * the first 1024 * floor(S / 1024) elements; every buffer 16-byte aligned.
  * Errors: ZS_EINVAL, ZS_EALIAS, ZS_EUNSUPPORTED as zs_adamw_step.
  */
 zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w, int64_t S,

@@ -1,6 +1,8 @@
 """The measurement aid zs_stream_ceiling writes the documented placeholders
-(p + m, v, p, XOR of the contributions' 16-byte vectors) over the first
-8 * floor(S / 8) elements and touches nothing else."""
+over the first 1024 * floor(S / 1024) elements (whole tile pairs) and touches
+nothing else: p + m into p, v into m, p into v, and into w the first two
+words of each 16-byte XOR of the contributions, in the lane maps of the
+fused kernel."""
 import numpy as np
 import pytest
 import torch
@@ -11,11 +13,31 @@ from gpu_util import device, to_np
 
 pytestmark = pytest.mark.gpu
 
+PAIR = 1024          # elements the kernel moves per wavefront and iteration
+
+
+def expected_w_words(words, dtype, L):
+    """u32 words of w[:L] from the contributions' u32 words (first L elements)."""
+    x = np.zeros_like(words[0])
+    for wd in words:
+        x ^= wd
+    if dtype == "f32":
+        # split map: lane vectors are 4 consecutive fp32 elements; the first two
+        # words of each XORed vector land in the 4 bf16 slots of w
+        return x.reshape(L // 4, 4)[:, :2].reshape(-1)
+    # bf16: per tile, lane l XORs words 4l .. 4l+3 (8 elements); LDS entry k
+    # holds lane k >> 1's vector, XORed with 1 when k is odd; w's elements
+    # 4k .. 4k+3 get the entry's first two words
+    xt = x.reshape(L // 512, 64, 4)
+    k = np.arange(128)
+    ent = xt[:, k >> 1, :2] ^ (k & 1).astype(np.uint32)[None, :, None]
+    return ent.reshape(-1)
+
 
 @pytest.mark.parametrize("dtype,n", [("bf16", 8), ("bf16", 3), ("f32", 4)])
-def test_stream_ceiling_placeholders(dtype, n):
+@pytest.mark.parametrize("S", [1024 * 39 + 69, 1024 * 38 + 512, 300])
+def test_stream_ceiling_placeholders(dtype, n, S):
     dev = device()
-    S = 8 * 5000 + 5
     p = W.master_init(S, 1, dev)
     m = W.master_init(S, 2, dev)
     v = W.master_init(S, 3, dev)
@@ -26,16 +48,15 @@ def test_stream_ceiling_placeholders(dtype, n):
     p0, m0, v0 = to_np(p), to_np(m), to_np(v)
     zs.zs_stream_ceiling(p, m, v, w, cs)
     torch.cuda.synchronize()
-    L = 8 * (S // 8)
+    L = PAIR * (S // PAIR)
     assert to_np(p)[:L].tobytes() == (p0[:L] + m0[:L]).astype(np.float32).tobytes()
     assert to_np(m)[:L].tobytes() == v0[:L].tobytes()
     assert to_np(v)[:L].tobytes() == p0[:L].tobytes()
     assert to_np(p)[L:].tobytes() == p0[L:].tobytes()
-    words = [np.ascontiguousarray(to_np(c)[:L]).view(np.uint32) for c in cs]
-    per_vec = 4 if dtype == "bf16" else 8          # u32 words per 8 elements of one contribution
-    x = np.zeros((L // 8, 4), np.uint32)
-    for wd in words:
-        blk = wd[:L // 8 * per_vec].reshape(L // 8, per_vec // 4, 4)
-        for h in range(per_vec // 4):
-            x ^= blk[:, h, :]
-    assert np.ascontiguousarray(to_np(w)[:L]).view(np.uint32).tobytes() == x.reshape(-1).tobytes()
+    assert to_np(m)[L:].tobytes() == m0[L:].tobytes()
+    assert to_np(v)[L:].tobytes() == v0[L:].tobytes()
+    assert not to_np(w)[L:].any()
+    if L:
+        words = [np.ascontiguousarray(to_np(c)[:L]).view(np.uint32) for c in cs]
+        want = expected_w_words(words, dtype, L)
+        assert np.ascontiguousarray(to_np(w)[:L]).view(np.uint32).tobytes() == want.tobytes()

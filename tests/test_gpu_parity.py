@@ -199,6 +199,32 @@ def test_adamw_vs_oracle(code, D):
         run_steps(D, S, code, 3, dev, seed=D)
 
 
+# The tiled kernels take two adjacent 512-element tiles per wavefront and
+# iteration; an odd last tile and the S % 512 tail go to the last workgroup.
+# Sizes around those edges, and one past the persistent grid (the tile-pair
+# loop wraps).
+TILE_EDGE_SIZES = (511, 512, 513, 1024, 1536, 1537, 3 * 1024 + 511, 2_500_517)
+
+
+@pytest.mark.parametrize("code,D", [(zs.ZS_BF16, 8), (zs.ZS_F32, 4), (zs.ZS_BF16, 3)])
+def test_adamw_tile_edges(code, D):
+    dev = device()
+    for S in TILE_EDGE_SIZES:
+        run_steps(D, S, code, 2, dev, seed=S % 101)
+
+
+@pytest.mark.parametrize("code,D", [(zs.ZS_BF16, 8), (zs.ZS_F32, 4), (zs.ZS_F32, 5)])
+def test_reduce_tile_edges(code, D):
+    dev = device()
+    gen = bf16_contribs if code == zs.ZS_BF16 else f32_contribs
+    for S in TILE_EDGE_SIZES:
+        cs = gen(D, S, S % 89, dev)
+        out = torch.empty(S, device=dev)
+        zs.zs_reduce_shard(cs, out)
+        want = O.reduce_shard([to_np(c) for c in cs], oracle_dtype(code))
+        check_f32(to_np(out), want, f"reduce D={D} S={S}", exact=True)
+
+
 def test_adamw_many_steps_gpt3m_shard():
     """The 3.3M GPT rank shard (S = 820,352), D = 4, all 10 steps."""
     run_steps(4, 820_352, zs.ZS_BF16, 10, device(), seed=5)
