@@ -212,6 +212,43 @@ def hybrid_leg(zs, torch, W, dev, hp, steps: int, arenas):
     return res
 
 
+def hbm_directions(zs, torch, dev, read_bytes: int, write_bytes: int):
+    """HBM's own rates for one direction at a time (zs_hbm_probe: reads,
+    writes and a copy over a 4 GiB buffer, the best of 1-4 workgroups per CU)
+    and the rate the step's mix of read_bytes and write_bytes per param would
+    reach if reads and writes overlapped perfectly at those rates."""
+    n = 4 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    zs.zs_hbm_probe(zs.ZS_PROBE_WRITE, a)
+    torch.cuda.synchronize()
+    best = {}
+    for name, kind, moved in (("read", zs.ZS_PROBE_READ, n), ("write", zs.ZS_PROBE_WRITE, n),
+                              ("copy", zs.ZS_PROBE_COPY, 2 * n)):
+        for per_cu in (1, 2, 3, 4):
+            dst = b[:16] if kind == zs.ZS_PROBE_READ else (b if kind == zs.ZS_PROBE_COPY else None)
+            ms = []
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                zs.zs_hbm_probe(kind, a, dst, blocks_per_cu=per_cu)
+                e1.record()
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            rate = moved / (min(ms) / 1e3) / 1e9
+            if rate > best.get(name, (0.0, 0))[0]:
+                best[name] = (rate, per_cu)
+    del a, b
+    torch.cuda.empty_cache()
+    rd, wr = best["read"][0], best["write"][0]
+    bound = (read_bytes + write_bytes) / (read_bytes / rd + write_bytes / wr)
+    return {"read_GB_s": rd, "read_blocks_per_cu": best["read"][1],
+            "write_GB_s": wr, "write_blocks_per_cu": best["write"][1],
+            "copy_GB_s": best["copy"][0], "copy_blocks_per_cu": best["copy"][1],
+            "step_mix": f"{read_bytes} B read + {write_bytes} B written per param",
+            "ideal_overlap_bound_GB_s": bound}
+
+
 def configs_leg(zs, torch, W, dev, hp, launches: int, arenas):
     """The fused reduce + AdamW kernel alone on the rank shards of the other
     workloads (one launch over each whole shard, contributions resident):
@@ -414,8 +451,12 @@ def main() -> int:
                     help="skip the HYBRID_SHARD (4 nodes x 8 GPUs, LLaMA-7B) step leg")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the per-bucket streamed (overlapped) step leg")
+    ap.add_argument("--no-copy", action="store_true",
+                    help="skip the plain 4 GiB device copy (the copy ceiling and the HBM "
+                         "counter calibration)")
     ap.add_argument("--copy-calibrate", action="store_true",
-                    help="also run a plain 4 GiB device copy (HBM counter calibration)")
+                    help="no effect: the copy runs unless --no-copy (accepted so that the "
+                         "recorded counter commands still run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the shard step is measured on one GPU only (asked for --gpus {args.gpus}); the "
@@ -599,10 +640,16 @@ def main() -> int:
         "wrap": {"pack_block_unit_f32_ms": pack_ms,
                  "pack_GB_s": pack_bytes / (pack_ms / 1e3) / 1e9},
     }
-    if args.copy_calibrate:
+    if not args.no_ceiling:
+        log("HBM direction probes: reads, writes and a copy alone")
+        dirs = hbm_directions(zs, torch, dev, read_bytes=28, write_bytes=14)
+        dirs["fused_over_bound"] = achieved / dirs["ideal_overlap_bound_GB_s"]
+        out["roofline"]["hbm_directions"] = dirs
+    if not args.no_copy:
         a = torch.empty(1 << 30, device=dev)          # 4 GiB fp32
         bb = torch.empty_like(a)
         a.fill_(1.0)
+        bb.copy_(a)                                   # warm
         torch.cuda.synchronize()
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record()

@@ -97,6 +97,7 @@ def load() -> ctypes.CDLL:
                 "zs_reshard": (i32, [P(vp), i32, i64, i64, i32, P(vp), i32, i64, vp]),
                 "zs_adamw_step_host": (i32, [vp, vp, vp, vp, i64, vp, P(zs_adamw_hp), i32]),
                 "zs_stream_ceiling": (i32, [vp, vp, vp, vp, i64, P(vp), i32, i32, vp]),
+                "zs_hbm_probe": (i32, [i32, vp, vp, i64, i32, vp]),
                 "zs_offload_step": (i32, [P(vp), i32, i32, i64, vp, vp, vp, vp, vp, vp, vp,
                                           P(zs_adamw_hp), i32, i64, vp, vp]),
                 "zs_shard_save": (i32, [ctypes.c_char_p, P(zs_shard_info), vp, vp, vp, vp, vp]),
@@ -503,6 +504,28 @@ def zs_stream_ceiling(p, m, v, w, contribs: Sequence, stream=None) -> None:
             raise ValueError("contributions must share one dtype and hold S elements")
     _check(load().zs_stream_ceiling(*ptrs, S, _ptr_array(contribs), len(contribs), code,
                                     _stream(p, stream)))
+
+
+ZS_PROBE_READ, ZS_PROBE_WRITE, ZS_PROBE_COPY = 0, 1, 2
+
+
+def zs_hbm_probe(kind: int, buf, buf2=None, blocks_per_cu: int = 1, stream=None) -> None:
+    """Measurement aid: read, write or copy all of buf (any dtype; its byte
+    size a multiple of 16) with the library's streaming access pattern.
+    buf2: the copy's destination (at least as large as buf), or a 16-byte
+    sink for a read."""
+    _dev(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if buf2 is not None:
+        _dev(buf2, "buf2")
+        need = nbytes if kind == ZS_PROBE_COPY else 16
+        if buf2.numel() * buf2.element_size() < need:
+            raise ValueError(f"buf2 must hold at least {need} bytes")
+    elif kind != ZS_PROBE_WRITE:
+        raise ValueError("buf2 is required for read and copy")
+    _check(load().zs_hbm_probe(int(kind), buf.data_ptr(),
+                               buf2.data_ptr() if buf2 is not None else None, nbytes,
+                               int(blocks_per_cu), _stream(buf, stream)))
 
 
 # Raw-pointer forms, for callers that manage device memory themselves.

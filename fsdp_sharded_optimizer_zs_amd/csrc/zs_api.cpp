@@ -133,7 +133,7 @@ using namespace zs;
 
 ZS_EXPORT const char* zs_last_error(void) { return g_last_error.c_str(); }
 
-ZS_EXPORT int32_t zs_abi_version(void) { return 105; }
+ZS_EXPORT int32_t zs_abi_version(void) { return 106; }
 
 ZS_EXPORT zs_status zs_unit_layout(const int64_t* numels, int32_t T, int32_t D,
                                    int64_t* offsets_out, int64_t* n_out, int64_t* n_pad_out,
@@ -391,7 +391,7 @@ ZS_EXPORT zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w,
     if (es == 0) return fail(ZS_EUNSUPPORTED, "%s: unknown dtype %d", who, dtype);
     if (n < 1 || n > ZS_MAX_D) return fail(ZS_EINVAL, "%s: n = %d outside 1..%d", who, n, ZS_MAX_D);
     if (!size_ok(S, 4)) return fail(ZS_EINVAL, "%s: S = %lld out of range", who, (long long)S);
-    if (S < 8) return ok();
+    if (S < 1024) return ok();
     if (!p || !m || !v || !w) return fail(ZS_EINVAL, "%s: p, m, v or w is NULL", who);
     if (!aligned(p, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(w, 16))
         return fail(ZS_EINVAL, "%s: p, m, v and w must be 16-byte aligned", who);
@@ -407,4 +407,28 @@ ZS_EXPORT zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w,
                 return fail(ZS_EALIAS, "%s: contribution %d overlaps an output", who, q);
     }
     return hip_status(launch_streams(p, m, v, w, S, cp, n, dtype, stream), who);
+}
+
+ZS_EXPORT zs_status zs_hbm_probe(int32_t kind, void* buf, void* buf2, int64_t bytes,
+                                 int32_t blocks_per_cu, hipStream_t stream) {
+    const char* who = "zs_hbm_probe";
+    if (kind != ZS_PROBE_READ && kind != ZS_PROBE_WRITE && kind != ZS_PROBE_COPY)
+        return fail(ZS_EINVAL, "%s: unknown kind %d", who, kind);
+    if (blocks_per_cu < 1 || blocks_per_cu > 16)
+        return fail(ZS_EINVAL, "%s: blocks_per_cu = %d outside 1..16", who, blocks_per_cu);
+    if (bytes < 0 || bytes % 16 != 0 || !size_ok(bytes / 16, 16))
+        return fail(ZS_EINVAL, "%s: bytes = %lld is not a non-negative multiple of 16", who,
+                    (long long)bytes);
+    if (bytes == 0) return ok();
+    if (buf == nullptr || !aligned(buf, 16))
+        return fail(ZS_EINVAL, "%s: buf is NULL or not 16-byte aligned", who);
+    const bool two = kind != ZS_PROBE_WRITE;
+    if (two) {
+        if (buf2 == nullptr || !aligned(buf2, 16))
+            return fail(ZS_EINVAL, "%s: buf2 is NULL or not 16-byte aligned", who);
+        const int64_t n2 = kind == ZS_PROBE_COPY ? bytes : 16;
+        if (overlap(range_of(buf, bytes, 1), range_of(buf2, n2, 1)))
+            return fail(ZS_EALIAS, "%s: buf and buf2 overlap", who);
+    }
+    return hip_status(launch_probe(kind, buf, buf2, bytes / 16, blocks_per_cu, stream), who);
 }

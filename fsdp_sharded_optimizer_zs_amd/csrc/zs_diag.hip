@@ -112,6 +112,41 @@ streams_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__
         tiles<BF16, kPair>(p4, m4, v4, w2, c, n, q * kPair, lane, xpose[wave]);
 }
 
+// Single-direction and copy streams over one buffer, for the memory system's
+// own rates: reads (two 16-byte vectors per lane in flight), writes (one
+// 16-byte vector per lane) and a copy, all non-temporal, in the grid-stride
+// order of the step kernels. nvec counts 16-byte vectors.
+__global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4* __restrict__ a,
+                                                              int64_t nvec,
+                                                              u32x4* __restrict__ sink) {
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    for (; i + stride < nvec; i += 2 * stride) {
+        const u32x4 x = __builtin_nontemporal_load(a + i);
+        const u32x4 y = __builtin_nontemporal_load(a + i + stride);
+        acc ^= x ^ y;
+    }
+    if (i < nvec) acc ^= __builtin_nontemporal_load(a + i);
+    // keeps the loads; taken only when every lane's XOR is one particular value
+    if ((acc.x & acc.y & acc.z & acc.w) == 0xffffffffu) sink[0] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void probe_write_kernel(u32x4* __restrict__ b,
+                                                               int64_t nvec) {
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride)
+        __builtin_nontemporal_store(u32x4{uint32_t(i), uint32_t(i >> 32), 0x5a5a5a5au, 0u}, b + i);
+}
+
+__global__ __launch_bounds__(kThreads) void probe_copy_kernel(const u32x4* __restrict__ a,
+                                                              u32x4* __restrict__ b,
+                                                              int64_t nvec) {
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(a + i), b + i);
+}
+
 }  // namespace
 
 hipError_t launch_streams(float* p, float* m, float* v, uint16_t* w, int64_t S,
@@ -127,6 +162,24 @@ hipError_t launch_streams(float* p, float* m, float* v, uint16_t* w, int64_t S,
     else
         hipLaunchKernelGGL((streams_kernel<false>), dim3(unsigned(blocks)), dim3(kThreads), 0,
                            stream, p, m, v, w, npairs, contribs, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe(int kind, void* buf, void* buf2, int64_t nvec, int per_cu,
+                        hipStream_t stream) {
+    const int64_t cap = int64_t(device_info().cu_count) * per_cu;
+    int64_t blocks = (nvec + kThreads - 1) / kThreads;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    const dim3 grid{unsigned(blocks)}, block{unsigned(kThreads)};
+    u32x4* a = static_cast<u32x4*>(buf);
+    u32x4* b = static_cast<u32x4*>(buf2);
+    if (kind == ZS_PROBE_READ)
+        hipLaunchKernelGGL(probe_read_kernel, grid, block, 0, stream, a, nvec, b);
+    else if (kind == ZS_PROBE_WRITE)
+        hipLaunchKernelGGL(probe_write_kernel, grid, block, 0, stream, a, nvec);
+    else
+        hipLaunchKernelGGL(probe_copy_kernel, grid, block, 0, stream, a, b, nvec);
     return hipGetLastError();
 }
 

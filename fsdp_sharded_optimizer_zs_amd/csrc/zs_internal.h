@@ -78,6 +78,8 @@ hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es,
                          void* flat, hipStream_t stream);
 hipError_t launch_streams(float* p, float* m, float* v, uint16_t* w, int64_t S,
                           const PtrPack& contribs, int n, int dtype, hipStream_t stream);
+hipError_t launch_probe(int kind, void* buf, void* buf2, int64_t nvec, int per_cu,
+                        hipStream_t stream);
 hipError_t launch_reshard(const PtrPack& src, int64_t S, const PtrPack& dst, int D2, int64_t S2,
                           int64_t N, int es, hipStream_t stream);
 

@@ -18,6 +18,9 @@
  *                    per-rank shard checkpoints, resumable at any D2
  *   zs_adamw_step_host, zs_offload_step
  *                    the step's AdamW on host cores (ZeRO-Offload)
+ *   zs_stream_ceiling, zs_hbm_probe
+ *                    measurement aids: the step's memory streams without its
+ *                    arithmetic, and HBM's rate for one direction alone
  *
  * Sources (web pages, by title and section):
  *   [ZT]   "7.10 -- Fully-sharded data parallel (FSDP / ZeRO-3)", AI / ML
@@ -456,6 +459,29 @@ zs_status zs_offload_step(const void* const* contribs, int32_t D, int32_t dtype,
 zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w, int64_t S,
                             const void* const* contribs, int32_t n, int32_t dtype,
                             hipStream_t stream);
+
+/*
+ * zs_hbm_probe -- a measurement aid, not part of the step: the memory
+ * system's own rate for one stream direction, so that the step kernel's mix
+ * of reads and writes can be read against what HBM gives each direction
+ * alone. Non-temporal 16-byte vector accesses in grid-stride order on a
+ * persistent grid of blocks_per_cu 256-thread workgroups per CU:
+ *
+ *   ZS_PROBE_READ   reads bytes of buf (two vectors per lane in flight); may
+ *                   write 16 bytes at buf2 (a sink that keeps the loads)
+ *   ZS_PROBE_WRITE  writes bytes of buf (element i of each 16-byte vector v:
+ *                   {v mod 2^32, v >> 32, 0x5a5a5a5a, 0} as uint32 words)
+ *   ZS_PROBE_COPY   copies bytes of buf to buf2
+ *
+ *   bytes           a multiple of 16; 0 returns ZS_OK with no launch
+ *   buf, buf2       16-byte aligned device pointers; buf2 unused for WRITE;
+ *                   for READ and COPY buf2 must not overlap buf
+ *   blocks_per_cu   1..16
+ * Errors: ZS_EINVAL (kind, sizes, alignment, NULL), ZS_EALIAS, ZS_EHIP.
+ */
+enum { ZS_PROBE_READ = 0, ZS_PROBE_WRITE = 1, ZS_PROBE_COPY = 2 };
+zs_status zs_hbm_probe(int32_t kind, void* buf, void* buf2, int64_t bytes,
+                       int32_t blocks_per_cu, hipStream_t stream);
 
 /* Text of the calling thread's most recent failure ("" if none). The pointer
  * stays valid until the thread's next call into the library. */

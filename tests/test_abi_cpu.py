@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
               "zs_gather_unit", "zs_step_pipelined", "zs_reduce_shard_ex", "zs_adamw_step_ex",
               "zs_reshard", "zs_shard_save", "zs_shard_info_read", "zs_shard_load",
               "zs_shard_load_resharded", "zs_adamw_step_host", "zs_offload_step",
-              "zs_stream_ceiling", "zs_last_error", "zs_abi_version"):
+              "zs_stream_ceiling", "zs_hbm_probe", "zs_last_error", "zs_abi_version"):
         assert n in names
 
 
@@ -360,3 +360,21 @@ def test_shard_save_and_load_argument_errors(lib, tmp_path):
     arr = (ctypes.c_char_p * 1)(p)
     assert lib.zs_shard_load_resharded(arr, 1, 2, 2, A, A + 0x1000, A + 0x2000, A + 0x3000, 10,
                                        None, None) == zs.ZS_EINVAL   # rank >= D2
+
+
+def test_hbm_probe_argument_errors(lib):
+    probe = lib.zs_hbm_probe
+    assert probe(3, A, A + (1 << 20), 1 << 20, 1, None) == zs.ZS_EINVAL          # kind
+    assert probe(zs.ZS_PROBE_READ, A, A + (1 << 20), 1 << 20, 0, None) == zs.ZS_EINVAL
+    assert probe(zs.ZS_PROBE_READ, A, A + (1 << 20), 1 << 20, 17, None) == zs.ZS_EINVAL
+    assert probe(zs.ZS_PROBE_WRITE, A, None, 100, 1, None) == zs.ZS_EINVAL        # not 16k
+    assert probe(zs.ZS_PROBE_WRITE, A, None, -16, 1, None) == zs.ZS_EINVAL
+    assert probe(zs.ZS_PROBE_WRITE, None, None, 1 << 20, 1, None) == zs.ZS_EINVAL
+    assert probe(zs.ZS_PROBE_WRITE, A + 8, None, 1 << 20, 1, None) == zs.ZS_EINVAL
+    assert probe(zs.ZS_PROBE_COPY, A, None, 1 << 20, 1, None) == zs.ZS_EINVAL
+    assert probe(zs.ZS_PROBE_COPY, A, A + 4, 1 << 20, 1, None) == zs.ZS_EINVAL     # misaligned
+    assert probe(zs.ZS_PROBE_COPY, A, A + 4096, 1 << 20, 1, None) == zs.ZS_EALIAS
+    assert "overlap" in zs.zs_last_error()
+    assert probe(zs.ZS_PROBE_READ, A, A + 64, 1 << 20, 1, None) == zs.ZS_EALIAS    # sink inside buf
+    assert probe(zs.ZS_PROBE_COPY, A, A + 4096, 0, 1, None) == zs.ZS_OK            # nothing to do
+

@@ -60,3 +60,31 @@ def test_stream_ceiling_placeholders(dtype, n, S):
         words = [np.ascontiguousarray(to_np(c)[:L]).view(np.uint32) for c in cs]
         want = expected_w_words(words, dtype, L)
         assert np.ascontiguousarray(to_np(w)[:L]).view(np.uint32).tobytes() == want.tobytes()
+
+
+@pytest.mark.parametrize("per_cu", [1, 3])
+def test_hbm_probe_write_copy_read(per_cu):
+    dev = device()
+    n = (1 << 20) + 48                                  # bytes, a multiple of 16
+    guard = 4096
+    big = torch.zeros(n + guard, dtype=torch.uint8, device=dev)
+    zs.zs_hbm_probe(zs.ZS_PROBE_WRITE, big[:n], blocks_per_cu=per_cu)
+    torch.cuda.synchronize()
+    words = to_np(big[:n].view(torch.int32)).view(np.uint32).reshape(-1, 4)
+    vec = np.arange(n // 16, dtype=np.uint64)
+    assert np.array_equal(words[:, 0], (vec & 0xffffffff).astype(np.uint32))
+    assert np.array_equal(words[:, 1], (vec >> 32).astype(np.uint32))
+    assert np.all(words[:, 2] == 0x5a5a5a5a) and np.all(words[:, 3] == 0)
+    assert not to_np(big[n:]).any()
+
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev)
+    dst = torch.zeros(n + guard, dtype=torch.uint8, device=dev)
+    zs.zs_hbm_probe(zs.ZS_PROBE_COPY, src, dst[:n], blocks_per_cu=per_cu)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src) and not to_np(dst[n:]).any()
+
+    before = src.clone()
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    zs.zs_hbm_probe(zs.ZS_PROBE_READ, src, sink, blocks_per_cu=per_cu)
+    torch.cuda.synchronize()
+    assert torch.equal(src, before)
