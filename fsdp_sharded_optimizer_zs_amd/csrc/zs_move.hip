@@ -89,9 +89,9 @@ template <int ES>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const zs_tensor_ref* __restrict__ table,
                                                         int T, int64_t N, PtrPack shards,
                                                         int64_t S, int64_t per_shard,
-                                                        int64_t items) {
+                                                        int64_t q0, int64_t q1) {
     using Tv = typename Elem<ES>::T;
-    for (int64_t q = blockIdx.x; q < items; q += gridDim.x) {
+    for (int64_t q = q0 + blockIdx.x; q < q1; q += gridDim.x) {
         const int64_t r = q / per_shard;
         const int64_t base = r * S;
         const int64_t lo = base + (q - r * per_shard) * kPackChunk;
@@ -124,19 +124,19 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const zs_tensor_ref* __r
     }
 }
 
-// Gather: the whole grid copies shard 0 to flat[0, S), then shard 1 to
-// flat[S, 2S), and so on. Walking the shards in order keeps one read and one
-// write stream open at a time; giving each shard its own slice of the grid
-// (all D copies at once) measured 8% slower on the 70B units, 5.43 against
-// 5.87 TB/s with the non-temporal stores.
+// One shard of a gather: the whole grid copies src[0, n) to dst[0, n).
+// launch_gather issues one such launch per shard, in shard order, so that
+// one read and one write stream are open at a time and every wavefront
+// starts each shard together: on the 70B units this ran at 6.15-6.17 TB/s
+// against 5.44-5.46 for a single launch walking all shards in order (whose
+// wavefronts drift apart across shard boundaries) and 5.43 for a single
+// launch giving each shard its own slice of the grid.
 template <int ES>
-__global__ __launch_bounds__(kThreads) void gather_kernel(PtrPack shards, int D, int64_t S,
-                                                          char* __restrict__ flat) {
+__global__ __launch_bounds__(kThreads) void copy_kernel(const char* __restrict__ src, int64_t n,
+                                                        char* __restrict__ dst) {
     const int64_t tid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
     const int64_t nthr = int64_t(gridDim.x) * kThreads;
-    for (int r = 0; r < D; ++r)
-        copy_run<ES>(flat + int64_t(r) * S * ES, static_cast<const char*>(shards.p[r]), S, tid,
-                     nthr);
+    copy_run<ES>(dst, src, n, tid, nthr);
 }
 
 // Re-shard: work item q covers new-flat [lo, hi) inside new shard r2 =
@@ -145,9 +145,10 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(PtrPack shards, int D,
 template <int ES>
 __global__ __launch_bounds__(kThreads) void reshard_kernel(PtrPack src, int64_t S, PtrPack dst,
                                                            int64_t S2, int64_t N,
-                                                           int64_t per_shard, int64_t items) {
+                                                           int64_t per_shard, int64_t q0,
+                                                           int64_t q1) {
     using Tv = typename Elem<ES>::T;
-    for (int64_t q = blockIdx.x; q < items; q += gridDim.x) {
+    for (int64_t q = q0 + blockIdx.x; q < q1; q += gridDim.x) {
         const int64_t r2 = q / per_shard;
         const int64_t base2 = r2 * S2;
         const int64_t lo = base2 + (q - r2 * per_shard) * kPackChunk;
@@ -169,36 +170,47 @@ __global__ __launch_bounds__(kThreads) void reshard_kernel(PtrPack src, int64_t 
 
 }  // namespace
 
+// Pack and re-shard: one launch per destination shard (the work items of
+// shard r are [r * per_shard, (r + 1) * per_shard)), in shard order, for the
+// same reason as the gather's launch per shard.
 hipError_t launch_reshard(const PtrPack& src, int64_t S, const PtrPack& dst, int D2, int64_t S2,
                           int64_t N, int es, hipStream_t stream) {
     const int64_t per_shard = (S2 + kPackChunk - 1) / kPackChunk;
-    const int64_t items = per_shard * D2;
     int64_t blocks = int64_t(device_info().cu_count) * ZS_MOVE_BLOCKS_PER_CU;
-    if (blocks > items) blocks = items;
+    if (blocks > per_shard) blocks = per_shard;
     if (blocks < 1) blocks = 1;
-    if (es == 2)
-        hipLaunchKernelGGL((reshard_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                           src, S, dst, S2, N, per_shard, items);
-    else
-        hipLaunchKernelGGL((reshard_kernel<4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                           src, S, dst, S2, N, per_shard, items);
-    return hipGetLastError();
+    for (int r = 0; r < D2; ++r) {
+        const int64_t q0 = r * per_shard, q1 = q0 + per_shard;
+        if (es == 2)
+            hipLaunchKernelGGL((reshard_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+                               stream, src, S, dst, S2, N, per_shard, q0, q1);
+        else
+            hipLaunchKernelGGL((reshard_kernel<4>), dim3(unsigned(blocks)), dim3(kThreads), 0,
+                               stream, src, S, dst, S2, N, per_shard, q0, q1);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es, int D,
                        const PtrPack& shards, int64_t S, hipStream_t stream) {
     const int64_t per_shard = (S + kPackChunk - 1) / kPackChunk;
-    const int64_t items = per_shard * D;
     int64_t blocks = int64_t(device_info().cu_count) * ZS_MOVE_BLOCKS_PER_CU;
-    if (blocks > items) blocks = items;
+    if (blocks > per_shard) blocks = per_shard;
     if (blocks < 1) blocks = 1;
-    if (es == 2)
-        hipLaunchKernelGGL((pack_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                           d_table, T, N, shards, S, per_shard, items);
-    else
-        hipLaunchKernelGGL((pack_kernel<4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                           d_table, T, N, shards, S, per_shard, items);
-    return hipGetLastError();
+    for (int r = 0; r < D; ++r) {
+        const int64_t q0 = r * per_shard, q1 = q0 + per_shard;
+        if (es == 2)
+            hipLaunchKernelGGL((pack_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                               d_table, T, N, shards, S, per_shard, q0, q1);
+        else
+            hipLaunchKernelGGL((pack_kernel<4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                               d_table, T, N, shards, S, per_shard, q0, q1);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es, void* flat,
@@ -209,13 +221,19 @@ hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es, void* 
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     char* f = static_cast<char*>(flat);
-    if (es == 2)
-        hipLaunchKernelGGL((gather_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                           shards, D, S, f);
-    else
-        hipLaunchKernelGGL((gather_kernel<4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                           shards, D, S, f);
-    return hipGetLastError();
+    for (int r = 0; r < D; ++r) {
+        const char* src = static_cast<const char*>(shards.p[r]);
+        char* dst = f + int64_t(r) * S * es;
+        if (es == 2)
+            hipLaunchKernelGGL((copy_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                               src, S, dst);
+        else
+            hipLaunchKernelGGL((copy_kernel<4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                               src, S, dst);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace zs
