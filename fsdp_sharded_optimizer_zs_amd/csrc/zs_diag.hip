@@ -11,7 +11,7 @@
 // combined value moved to the split map (lane t: 4t..4t+3 and
 // 256+4t..256+4t+3) through LDS; fp32 contributions and p, m, v in the split
 // map; non-temporal contribution loads, temporal state loads, non-temporal
-// stores, a persistent grid of the same size. The values written are
+// stores, a grid of one wavefront per tile pair. The values written are
 // placeholders: p + m into p, v into m, p into v, and into w the first two
 // words of each 16-byte XOR of the contributions (bf16: taken after the LDS
 // exchange, the odd entries with 1 XORed into every word).
@@ -152,9 +152,8 @@ __global__ __launch_bounds__(kThreads) void probe_copy_kernel(const u32x4* __res
 hipError_t launch_streams(float* p, float* m, float* v, uint16_t* w, int64_t S,
                           const PtrPack& contribs, int n, int dtype, hipStream_t stream) {
     const int64_t npairs = S / (kPair * kTile);
-    const int64_t cap = int64_t(device_info().cu_count) * ZS_STEP_BLOCKS_PER_CU;
     int64_t blocks = (npairs + kWaves - 1) / kWaves;
-    if (blocks > cap) blocks = cap;
+    if (blocks > kMaxGrid) blocks = kMaxGrid;
     if (blocks < 1) blocks = 1;
     if (dtype == ZS_BF16)
         hipLaunchKernelGGL((streams_kernel<true>), dim3(unsigned(blocks)), dim3(kThreads), 0,

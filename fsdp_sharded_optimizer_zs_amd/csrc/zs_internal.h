@@ -7,22 +7,23 @@
 
 #include "../../include/zs.h"
 
-// Launch shape of the tiled step kernels (workgroups of 256 threads): tiles
-// per wavefront and iteration, and workgroups per CU for the persistent grid.
-// Two adjacent 512-element tiles per iteration with one workgroup per CU was
-// the fastest shape measured on MI355X: over the 81 buckets of a 70B rank
-// shard 6.05-6.11 TB/s, against 5.94-6.04 with single tiles and two
-// workgroups per CU, 5.74 with three tiles; equal or better too for 32- and
-// 16-contribution folds (the full LLaMA-7B shard at D = 32, the ragged fp32
-// unit at D = 16, the HYBRID_SHARD buckets).
+// Launch shape of the tiled step kernels (workgroups of 256 threads, 4
+// wavefronts): ZS_STEP_TILES adjacent 512-element tiles per wavefront, and one
+// wavefront per tile group: the grid covers the whole shard (up to
+// kMaxGrid workgroups; the kernels loop in grid-stride order past that).
+// Measured on MI355X over the 81 buckets of a 70B rank shard: 6.17 TB/s,
+// against 6.05-6.11 for a persistent grid of one workgroup per CU (whose
+// wavefronts drift apart over a long launch, so more HBM rows are open at
+// once), 6.09 with one tile per wavefront, 5.24 with four; equal or better
+// on the 16- and 32-contribution folds too.
 #ifndef ZS_STEP_TILES
 #define ZS_STEP_TILES 2
 #endif
-#ifndef ZS_STEP_BLOCKS_PER_CU
-#define ZS_STEP_BLOCKS_PER_CU 1
-#endif
 
 namespace zs {
+
+// Largest grid any kernel of the library is launched with.
+constexpr int64_t kMaxGrid = int64_t(1) << 24;
 
 // Up to ZS_MAX_D device pointers passed by value as a kernel argument.
 struct PtrPack {

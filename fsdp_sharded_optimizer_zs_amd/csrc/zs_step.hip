@@ -4,10 +4,9 @@
 // Both kernels are streaming, elementwise and HBM-bound: per element they
 // read the D gradient contributions (and p, m, v), do a few dozen VALU
 // operations and write the results once. There is no dense contraction, so
-// no MFMA. Work goes in 512-element tiles, 8 elements per lane; a wavefront
-// takes two adjacent tiles per iteration, and a persistent grid of one
-// workgroup per CU walks the tile pairs in grid-stride order. Inside a tile
-// two lane maps are used:
+// no MFMA. Work goes in 512-element tiles, 8 elements per lane; each
+// wavefront takes two adjacent tiles, and the grid has one wavefront per tile
+// pair. Inside a tile two lane maps are used:
 //
 //   run map:   lane t holds elements 8t .. 8t+7 (one 16-byte bf16 vector);
 //   split map: lane t holds elements 4t .. 4t+3 and 256+4t .. 256+4t+3 (two
@@ -21,9 +20,8 @@
 // the split map through a 2 KiB LDS slot per wavefront. (With the run map for
 // fp32 too, a lane's 32 bytes went out as two 16-byte stores and lines could
 // leave L2 half written: 3.6% more HBM writes. On MI355X's 70B buckets the
-// split map with tile pairs and one workgroup per CU runs the step at
-// 6.05-6.11 TB/s, against 5.94-6.04 for the run map with two workgroups per
-// CU.)
+// split map with tile pairs runs the step at 6.17 TB/s, against 5.94-6.04
+// for the run map on a persistent grid of two workgroups per CU.)
 //
 // The arithmetic follows the operation order fixed for the step exactly:
 // contributions widened exactly and folded left to right in rank order,
@@ -40,7 +38,8 @@
 // read-once contributions and non-temporal stores; the state p, m, v is
 // loaded with temporal loads, because non-temporal loads of lines that the
 // same lane then rewrites measured 20% slower (4.9 against 6.0 TB/s). The
-// launch shape (ZS_STEP_TILES, ZS_STEP_BLOCKS_PER_CU) is in zs_internal.h.
+// launch shape (ZS_STEP_TILES, one wavefront per tile group) is in
+// zs_internal.h.
 #ifndef ZS_NT_LOADS
 #define ZS_NT_LOADS 1
 #endif
@@ -63,10 +62,9 @@ constexpr int kTile = kWave * kVec;         // elements per wavefront tile
 
 // Occupancy the tiled kernels are compiled for: at most 2 wavefronts per
 // SIMD, so up to 256 VGPRs each and the scheduler issues a tile pair's 28
-// loads before their first use. Without it the compiler spends registers for
-// an occupancy the persistent grid never uses and serializes the loads
-// (3.5-5.9 TB/s on MI355X); at most 1 wavefront per SIMD keeps a second
-// workgroup off any CU, and the grid's last workgroups then wait (3.6 TB/s).
+// loads before their first use. Without it the compiler saves registers for
+// a higher occupancy and serializes the loads (3.5-5.9 TB/s on MI355X); at
+// most 1 wavefront per SIMD measured 3.3-3.6 TB/s.
 #ifndef ZS_WAVES
 #define ZS_WAVES __attribute__((amdgpu_waves_per_eu(1, 2)))
 #endif
@@ -441,15 +439,12 @@ __global__ __launch_bounds__(kThreads) void reduce_scalar_kernel(float* __restri
 // ---------------------------------------------------------------- dispatch
 
 // Workgroups for `lanes` lanes of work (elements for the scalar kernels,
-// tile groups x 64 for the tiled ones), capped at `per_cu` per CU.
-int grid_for(int64_t lanes, int per_cu) {
-    const int64_t cap = int64_t(device_info().cu_count) * per_cu;
+// tile groups x 64 for the tiled ones): one lane per unit of work.
+int grid_for(int64_t lanes) {
     int64_t blocks = (lanes + kThreads - 1) / kThreads;
-    if (blocks > cap) blocks = cap;
+    if (blocks > kMaxGrid) blocks = kMaxGrid;
     return blocks < 1 ? 1 : int(blocks);
 }
-
-constexpr int kScalarBlocksPerCu = 2;  // the element-at-a-time fallback kernels
 
 // What one launch computes: the AdamW step (out == nullptr) or the reduce
 // alone into out.
@@ -467,8 +462,8 @@ struct Job {
 template <int DT, class Sum>
 hipError_t launch_job(const Job& j, const PtrPack& c, const Sum& sum, hipStream_t stream) {
     constexpr int TP = ZS_STEP_TILES;
-    const int tiled = grid_for(j.S / (TP * kTile) * kWave, ZS_STEP_BLOCKS_PER_CU);
-    const int scalar = grid_for(j.S, kScalarBlocksPerCu);
+    const int tiled = grid_for(j.S / (TP * kTile) * kWave);
+    const int scalar = grid_for(j.S);
     if (j.out == nullptr) {
         if (j.aligned)
             hipLaunchKernelGGL((adamw_vec_kernel<DT, Sum, TP>), dim3(tiled), dim3(kThreads), 0,
