@@ -429,6 +429,30 @@ def unfused_leg(zs, torch, p, m, v, wshard, buckets, D, step_t, hp):
             "unfused_ms_per_step": red + ada, "bytes_per_param": 2 * D + 4 + 30}
 
 
+def in_place_leg(zs, torch, p, m, v, buckets, step_t, hp, steps: int = 3):
+    """The step with an in-place all-gather, as FSDP lays a unit out: the
+    rank's bf16 working shard is written by the step straight into its own
+    slot of the unit buffer (slot 0 for rank 0), and zs_gather_unit then
+    copies only the D - 1 peer shards. Wall time per step over the same 81
+    buckets, beside the main leg's out-of-place form."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for rep in range(2):
+        if rep:
+            torch.cuda.synchronize()
+            ev[0].record()
+        for t in range(steps if rep else 1):
+            h = zs.AdamWHP(step=step_t + t, **hp)
+            for sl, sz, cs, shards, ubuf in buckets:
+                slot = ubuf[:sz]
+                zs.zs_adamw_step(p[sl], m[sl], v[sl], slot, cs, h)
+                zs.zs_gather_unit([slot] + shards[1:], ubuf)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    S = sum(sz for _, sz, _, _, _ in buckets)
+    return {"ms_per_step": ms, "params_per_s": S / (ms / 1e3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -439,6 +463,8 @@ def main() -> int:
                     help="skip the unfused (reduce, then AdamW) form of the step")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the no-arithmetic stream ceiling on the same buckets")
+    ap.add_argument("--no-in-place", action="store_true",
+                    help="skip the step with an in-place all-gather")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the ZeRO-Offload (host-core AdamW) leg")
     ap.add_argument("--host-threads", type=int, default=16,
@@ -663,6 +689,11 @@ def main() -> int:
         log("unfused leg: zs_reduce_shard then zs_adamw_step on the same buckets")
         out["unfused"] = unfused_leg(zs, torch, p, m, v, wshard, buckets, D, args.warmup + K + 1, hp)
         out["unfused"]["fused_ms_per_step"] = adam_ms / K
+    if not args.no_in_place:
+        log("in-place leg: the working shard written into its slot of the unit buffer")
+        out["in_place_gather"] = in_place_leg(zs, torch, p, m, v, buckets,
+                                              args.warmup + K + 1, hp)
+        out["in_place_gather"]["main_ms_per_step"] = ms_per_step
     if not args.no_pipeline:
         log("pipeline leg: contributions streamed per bucket, overlapped with the step")
         out["pipeline"] = pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D,

@@ -343,11 +343,21 @@ ZS_EXPORT zs_status zs_gather_unit(const void* const* shards, int32_t D, int64_t
     PtrPack sp;
     zs_status st = take_ptrs(shards, D, es, "zs_gather_unit: shards", &sp);
     if (st != ZS_OK) return st;
+    // A shard sitting exactly in its own slot (in-place all-gather) is not
+    // copied; any other overlap with flat_out would read what a copy writes.
     const Range out = range_of(flat_out, S * D, es);
-    for (int r = 0; r < D; ++r)
+    char* const f = static_cast<char*>(flat_out);
+    uint64_t in_place = 0;
+    for (int r = 0; r < D; ++r) {
+        if (sp.p[r] == f + int64_t(r) * S * es) {
+            in_place |= uint64_t(1) << r;
+            continue;
+        }
         if (overlap(out, range_of(sp.p[r], S, es)))
             return fail(ZS_EALIAS, "zs_gather_unit: flat_out overlaps shard %d", r);
-    return hip_status(launch_gather(sp, D, S, es, flat_out, stream), "zs_gather_unit launch");
+    }
+    return hip_status(launch_gather(sp, D, S, es, flat_out, in_place, stream),
+                      "zs_gather_unit launch");
 }
 
 ZS_EXPORT zs_status zs_reshard(const void* const* src, int32_t D, int64_t S, int64_t N,

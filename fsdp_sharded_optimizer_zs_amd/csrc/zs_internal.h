@@ -75,8 +75,9 @@ hipError_t launch_reduce(const PtrPack& contribs, int nd, int R, bool rnd, int d
                          float inv_n, float* out, bool aligned, hipStream_t stream);
 hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es,
                        int D, const PtrPack& shards, int64_t S, hipStream_t stream);
-hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es,
-                         void* flat, hipStream_t stream);
+// in_place: bit r set when shard r already sits in its slot (not copied).
+hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es, void* flat,
+                         uint64_t in_place, hipStream_t stream);
 hipError_t launch_streams(float* p, float* m, float* v, uint16_t* w, int64_t S,
                           const PtrPack& contribs, int n, int dtype, hipStream_t stream);
 hipError_t launch_probe(int kind, void* buf, void* buf2, int64_t nvec, int per_cu,

@@ -210,13 +210,14 @@ hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es, i
 }
 
 hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es, void* flat,
-                         hipStream_t stream) {
+                         uint64_t in_place, hipStream_t stream) {
     const int64_t vecs = (S * es + 15) / 16 + 1;
     int64_t blocks = (vecs + kThreads - 1) / kThreads;
     if (blocks > kMaxGrid) blocks = kMaxGrid;
     if (blocks < 1) blocks = 1;
     char* f = static_cast<char*>(flat);
     for (int r = 0; r < D; ++r) {
+        if ((in_place >> r) & 1) continue;
         const char* src = static_cast<const char*>(shards.p[r]);
         char* dst = f + int64_t(r) * S * es;
         if (es == 2)

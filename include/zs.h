@@ -262,7 +262,11 @@ zs_status zs_adamw_step_ex(float* p, float* m, float* v, uint16_t* w_out, int64_
  *   S         >= 0
  *   dtype     ZS_BF16 or ZS_F32
  *   flat_out  device, D * S elements
- * Errors: ZS_EINVAL, ZS_EALIAS (flat_out overlaps a shard), ZS_EUNSUPPORTED.
+ * In place: a shard whose pointer is exactly flat_out + r * S (its own slot,
+ * as in an in-place all-gather, where each rank's shard lives inside the
+ * unit buffer) is already where it belongs and is not copied.
+ * Errors: ZS_EINVAL, ZS_EALIAS (a shard overlaps flat_out anywhere but
+ * exactly in its own slot), ZS_EUNSUPPORTED.
  */
 zs_status zs_gather_unit(const void* const* shards, int32_t D, int64_t S,
                          int32_t dtype, void* flat_out, hipStream_t stream);

@@ -153,6 +153,15 @@ def test_reduce_and_gather_argument_errors(lib):
     assert lib.zs_gather_unit(arr, 2, 100, zs.ZS_F32, A + 0x20001, None) == zs.ZS_EINVAL
     assert lib.zs_gather_unit(arr, 65, 100, zs.ZS_BF16, A + 0x20000, None) == zs.ZS_EINVAL
     assert lib.zs_gather_unit(arr, 2, 1 << 62, zs.ZS_BF16, A + 0x20000, None) == zs.ZS_EINVAL
+    # in place means exactly the shard's own slot; anything else overlapping flat_out is refused
+    F = A + 0x40000
+    off = (ctypes.c_void_p * 2)(F + 2, A)                # shard 0 one element past its slot
+    assert lib.zs_gather_unit(off, 2, 100, zs.ZS_BF16, F, None) == zs.ZS_EALIAS
+    swapped = (ctypes.c_void_p * 2)(A, F)                # shard 1 sitting in slot 0
+    assert lib.zs_gather_unit(swapped, 2, 100, zs.ZS_BF16, F, None) == zs.ZS_EALIAS
+    crossing = (ctypes.c_void_p * 2)(F, F + 100)         # shard 1 straddles slots (S = 100, es = 2)
+    assert lib.zs_gather_unit(crossing, 2, 100, zs.ZS_BF16, F, None) == zs.ZS_EALIAS
+    assert "shard 1" in zs.zs_last_error()
 
 
 def test_pack_argument_errors(lib):

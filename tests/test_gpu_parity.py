@@ -352,3 +352,26 @@ def test_errors_on_real_buffers():
         zs.zs_adamw_step(p, m, torch.zeros(S, device=dev), w, [c], zs.AdamWHP(step=0, **HP))
     assert e.value.status == zs.ZS_EINVAL
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", [torch.int16, torch.float32])
+def test_gather_in_place_shards(dtype):
+    """Shards that sit exactly in their own slot of the unit buffer (an
+    in-place all-gather) are left alone; the others are copied in; the result
+    equals the out-of-place gather."""
+    dev = device()
+    D, S = 8, 70001
+    src = [torch.randint(-30000, 30000, (S,), device=dev).to(dtype) for _ in range(D)]
+    want = torch.cat(src)
+    for in_place in ({0}, {0, 3, 7}, set(range(D))):
+        flat = torch.full((D * S,), -7, device=dev).to(dtype)
+        shards = []
+        for r in range(D):
+            if r in in_place:
+                flat[r * S:(r + 1) * S].copy_(src[r])
+                shards.append(flat[r * S:(r + 1) * S])
+            else:
+                shards.append(src[r])
+        zs.zs_gather_unit(shards, flat)
+        torch.cuda.synchronize()
+        assert torch.equal(flat, want), sorted(in_place)
