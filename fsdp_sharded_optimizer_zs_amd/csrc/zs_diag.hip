@@ -5,16 +5,14 @@
 // peak.
 //
 // Same launch shape, occupancy, tiles, lane maps, vector widths and cache
-// hints as the fused kernel: two adjacent 512-element tiles per wavefront and
-// iteration (whole pairs only);
-// bf16 contributions in the run map (lane t: elements 8t..8t+7), their
-// combined value moved to the split map (lane t: 4t..4t+3 and
-// 256+4t..256+4t+3) through LDS; fp32 contributions and p, m, v in the split
-// map; non-temporal contribution loads, temporal state loads, non-temporal
-// stores, a grid of one wavefront per tile pair. The values written are
-// placeholders: p + m into p, v into m, p into v, and into w the first two
-// words of each 16-byte XOR of the contributions (bf16: taken after the LDS
-// exchange, the odd entries with 1 XORed into every word).
+// hints as the fused kernel: two adjacent 512-element tiles per wavefront
+// (whole pairs only) and one wavefront per tile pair; bf16 contributions in
+// the run map (lane t: elements 8t..8t+7), their combined value moved to the
+// split map (lane t: 4t..4t+3 and 256+4t..256+4t+3) through LDS; fp32
+// contributions and p, m, v in the split map; non-temporal loads and stores.
+// The values written are placeholders: p + m into p, v into m, p into v, and
+// into w the first two words of each 16-byte XOR of the contributions (bf16:
+// taken after the LDS exchange, the odd entries with 1 XORed into every word).
 
 #include "zs_internal.h"
 
@@ -49,9 +47,9 @@ __device__ __forceinline__ void tiles(f32x4* __restrict__ p4, f32x4* __restrict_
 #pragma unroll
     for (int u = 0; u < TP; ++u) {
         const int64_t a = (tile0 + u) * (kTile / 4) + lane, b = a + kWave;
-        pa[u] = p4[a], pb[u] = p4[b];
-        ma[u] = m4[a], mb[u] = m4[b];
-        va[u] = v4[a], vb[u] = v4[b];
+        pa[u] = __builtin_nontemporal_load(p4 + a), pb[u] = __builtin_nontemporal_load(p4 + b);
+        ma[u] = __builtin_nontemporal_load(m4 + a), mb[u] = __builtin_nontemporal_load(m4 + b);
+        va[u] = __builtin_nontemporal_load(v4 + a), vb[u] = __builtin_nontemporal_load(v4 + b);
     }
     u32x4 sa[TP], sb[TP];
 #pragma unroll
