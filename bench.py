@@ -214,7 +214,8 @@ def hybrid_leg(zs, torch, W, dev, hp, steps: int, arenas):
 
 def hbm_directions(zs, torch, dev, read_bytes: int, write_bytes: int):
     """HBM's own rates for one direction at a time (zs_hbm_probe: reads,
-    writes and a copy over a 4 GiB buffer, the best of 1-4 workgroups per CU)
+    writes and a copy over a 4 GiB buffer, the best of a grid that covers the
+    buffer and persistent grids of 1-4 workgroups per CU)
     and the rate the step's mix of read_bytes and write_bytes per param would
     reach if reads and writes overlapped perfectly at those rates."""
     n = 4 << 30
@@ -225,7 +226,7 @@ def hbm_directions(zs, torch, dev, read_bytes: int, write_bytes: int):
     best = {}
     for name, kind, moved in (("read", zs.ZS_PROBE_READ, n), ("write", zs.ZS_PROBE_WRITE, n),
                               ("copy", zs.ZS_PROBE_COPY, 2 * n)):
-        for per_cu in (1, 2, 3, 4):
+        for per_cu in (0, 1, 2, 3, 4):
             dst = b[:16] if kind == zs.ZS_PROBE_READ else (b if kind == zs.ZS_PROBE_COPY else None)
             ms = []
             for _ in range(3):

@@ -424,8 +424,8 @@ ZS_EXPORT zs_status zs_hbm_probe(int32_t kind, void* buf, void* buf2, int64_t by
     const char* who = "zs_hbm_probe";
     if (kind != ZS_PROBE_READ && kind != ZS_PROBE_WRITE && kind != ZS_PROBE_COPY)
         return fail(ZS_EINVAL, "%s: unknown kind %d", who, kind);
-    if (blocks_per_cu < 1 || blocks_per_cu > 16)
-        return fail(ZS_EINVAL, "%s: blocks_per_cu = %d outside 1..16", who, blocks_per_cu);
+    if (blocks_per_cu < 0 || blocks_per_cu > 16)
+        return fail(ZS_EINVAL, "%s: blocks_per_cu = %d outside 0..16", who, blocks_per_cu);
     if (bytes < 0 || bytes % 16 != 0 || !size_ok(bytes / 16, 16))
         return fail(ZS_EINVAL, "%s: bytes = %lld is not a non-negative multiple of 16", who,
                     (long long)bytes);

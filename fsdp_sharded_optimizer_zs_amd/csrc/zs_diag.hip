@@ -164,8 +164,11 @@ hipError_t launch_streams(float* p, float* m, float* v, uint16_t* w, int64_t S,
 
 hipError_t launch_probe(int kind, void* buf, void* buf2, int64_t nvec, int per_cu,
                         hipStream_t stream) {
-    const int64_t cap = int64_t(device_info().cu_count) * per_cu;
-    int64_t blocks = (nvec + kThreads - 1) / kThreads;
+    // per_cu 0: a grid that covers the buffer (two vectors per lane for reads,
+    // one otherwise); else a persistent grid of per_cu workgroups per CU
+    const int64_t lanes = kind == ZS_PROBE_READ ? (nvec + 1) / 2 : nvec;
+    const int64_t cap = per_cu > 0 ? int64_t(device_info().cu_count) * per_cu : kMaxGrid;
+    int64_t blocks = (lanes + kThreads - 1) / kThreads;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     const dim3 grid{unsigned(blocks)}, block{unsigned(kThreads)};

@@ -123,18 +123,37 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const zs_tensor_ref* __r
     }
 }
 
-// One shard of a gather: the grid copies src[0, n) to dst[0, n). launch_gather
-// issues one such launch per shard, in shard order, so that one read and one
-// write stream are open at a time: on the 70B units this ran at 6.15-6.17
-// TB/s against 5.44-5.46 for a single persistent launch walking all shards in
-// order (whose wavefronts drift apart across shard boundaries) and 5.43 for a
-// single launch giving each shard its own slice of the grid.
+// Gather, general case (a shard, or a slot of the unit buffer, not 16-byte
+// aligned): one launch per shard, in shard order, the grid copying src[0, n)
+// to dst[0, n). When everything is aligned, gather_flat_kernel moves the
+// whole unit in one launch whose grid covers it, lane v on destination
+// vector v: on the 70B units 6.56 TB/s, against 6.22 for one launch per
+// shard (eight short launches, each with its own start and drain), 5.44-5.46
+// for a single persistent launch walking the shards in order (whose
+// wavefronts drift apart) and 5.43 for one persistent launch giving each
+// shard its own slice of the grid.
 template <int ES>
 __global__ __launch_bounds__(kThreads) void copy_kernel(const char* __restrict__ src, int64_t n,
                                                         char* __restrict__ dst) {
     const int64_t tid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
     const int64_t nthr = int64_t(gridDim.x) * kThreads;
     copy_run<ES>(dst, src, n, tid, nthr);
+}
+
+// Gather in one launch when every shard and slot is 16-byte aligned: lane v
+// of the grid moves destination vector v, which lies in slot r = v / nv
+// (nv vectors per shard); shards marked in place are left alone.
+__global__ __launch_bounds__(kThreads) void gather_flat_kernel(PtrPack shards, int64_t nv,
+                                                               int64_t total,
+                                                               u32x4* __restrict__ flat,
+                                                               uint64_t in_place) {
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    for (int64_t v = int64_t(blockIdx.x) * kThreads + threadIdx.x; v < total; v += stride) {
+        const int64_t r = v / nv;
+        if ((in_place >> r) & 1) continue;
+        const u32x4* src = static_cast<const u32x4*>(shards.p[r]);
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + (v - r * nv)), flat + v);
+    }
 }
 
 // Re-shard: work item q covers new-flat [lo, hi) inside new shard r2 =
@@ -211,6 +230,18 @@ hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es, i
 
 hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es, void* flat,
                          uint64_t in_place, hipStream_t stream) {
+    bool aligned = (reinterpret_cast<uintptr_t>(flat) & 15) == 0 && (S * es) % 16 == 0;
+    for (int r = 0; r < D && aligned; ++r)
+        aligned = (reinterpret_cast<uintptr_t>(shards.p[r]) & 15) == 0;
+    if (aligned) {
+        const int64_t nv = S * es / 16, total = nv * D;
+        int64_t blocks = (total + kThreads - 1) / kThreads;
+        if (blocks > kMaxGrid) blocks = kMaxGrid;
+        if (blocks < 1) blocks = 1;
+        hipLaunchKernelGGL(gather_flat_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                           shards, nv, total, reinterpret_cast<u32x4*>(flat), in_place);
+        return hipGetLastError();
+    }
     const int64_t vecs = (S * es + 15) / 16 + 1;
     int64_t blocks = (vecs + kThreads - 1) / kThreads;
     if (blocks > kMaxGrid) blocks = kMaxGrid;

@@ -468,8 +468,9 @@ zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w, int64_t S
  * zs_hbm_probe -- a measurement aid, not part of the step: the memory
  * system's own rate for one stream direction, so that the step kernel's mix
  * of reads and writes can be read against what HBM gives each direction
- * alone. Non-temporal 16-byte vector accesses in grid-stride order on a
- * persistent grid of blocks_per_cu 256-thread workgroups per CU:
+ * alone. Non-temporal 16-byte vector accesses in grid-stride order, on a
+ * grid of 256-thread workgroups that covers the buffer (blocks_per_cu = 0)
+ * or on a persistent grid of blocks_per_cu workgroups per CU:
  *
  *   ZS_PROBE_READ   reads bytes of buf (two vectors per lane in flight); may
  *                   write 16 bytes at buf2 (a sink that keeps the loads)
@@ -480,7 +481,7 @@ zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w, int64_t S
  *   bytes           a multiple of 16; 0 returns ZS_OK with no launch
  *   buf, buf2       16-byte aligned device pointers; buf2 unused for WRITE;
  *                   for READ and COPY buf2 must not overlap buf
- *   blocks_per_cu   1..16
+ *   blocks_per_cu   0..16
  * Errors: ZS_EINVAL (kind, sizes, alignment, NULL), ZS_EALIAS, ZS_EHIP.
  */
 enum { ZS_PROBE_READ = 0, ZS_PROBE_WRITE = 1, ZS_PROBE_COPY = 2 };

@@ -374,7 +374,7 @@ def test_shard_save_and_load_argument_errors(lib, tmp_path):
 def test_hbm_probe_argument_errors(lib):
     probe = lib.zs_hbm_probe
     assert probe(3, A, A + (1 << 20), 1 << 20, 1, None) == zs.ZS_EINVAL          # kind
-    assert probe(zs.ZS_PROBE_READ, A, A + (1 << 20), 1 << 20, 0, None) == zs.ZS_EINVAL
+    assert probe(zs.ZS_PROBE_READ, A, A + (1 << 20), 1 << 20, -1, None) == zs.ZS_EINVAL
     assert probe(zs.ZS_PROBE_READ, A, A + (1 << 20), 1 << 20, 17, None) == zs.ZS_EINVAL
     assert probe(zs.ZS_PROBE_WRITE, A, None, 100, 1, None) == zs.ZS_EINVAL        # not 16k
     assert probe(zs.ZS_PROBE_WRITE, A, None, -16, 1, None) == zs.ZS_EINVAL

@@ -62,7 +62,7 @@ def test_stream_ceiling_placeholders(dtype, n, S):
         assert np.ascontiguousarray(to_np(w)[:L]).view(np.uint32).tobytes() == want.tobytes()
 
 
-@pytest.mark.parametrize("per_cu", [1, 3])
+@pytest.mark.parametrize("per_cu", [0, 1, 3])
 def test_hbm_probe_write_copy_read(per_cu):
     dev = device()
     n = (1 << 20) + 48                                  # bytes, a multiple of 16

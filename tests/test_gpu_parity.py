@@ -360,10 +360,14 @@ def test_gather_in_place_shards(dtype):
     in-place all-gather) are left alone; the others are copied in; the result
     equals the out-of-place gather."""
     dev = device()
-    D, S = 8, 70001
+    for S in (70001, 70000):            # a general (per-shard) and an aligned (one-launch) gather
+        _gather_in_place_case(dev, dtype, 8, S)
+
+
+def _gather_in_place_case(dev, dtype, D, S):
     src = [torch.randint(-30000, 30000, (S,), device=dev).to(dtype) for _ in range(D)]
     want = torch.cat(src)
-    for in_place in ({0}, {0, 3, 7}, set(range(D))):
+    for in_place in (set(), {0}, {0, 3, 7}, set(range(D))):
         flat = torch.full((D * S,), -7, device=dev).to(dtype)
         shards = []
         for r in range(D):
@@ -374,4 +378,4 @@ def test_gather_in_place_shards(dtype):
                 shards.append(src[r])
         zs.zs_gather_unit(shards, flat)
         torch.cuda.synchronize()
-        assert torch.equal(flat, want), sorted(in_place)
+        assert torch.equal(flat, want), (S, sorted(in_place))
