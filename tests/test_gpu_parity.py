@@ -379,3 +379,20 @@ def _gather_in_place_case(dev, dtype, D, S):
         zs.zs_gather_unit(shards, flat)
         torch.cuda.synchronize()
         assert torch.equal(flat, want), (S, sorted(in_place))
+
+
+def test_gather_in_place_d64_last_shard():
+    """The in-place mask at its widest: D = 64 with shard 63 (the mask's top
+    bit) and shard 0 in place, both gather paths."""
+    dev = device()
+    for S in (1000, 1001):
+        D = 64
+        src = [torch.randint(-30000, 30000, (S,), device=dev).to(torch.int16) for _ in range(D)]
+        flat = torch.full((D * S,), -7, dtype=torch.int16, device=dev)
+        shards = list(src)
+        for r in (0, 63):
+            flat[r * S:(r + 1) * S].copy_(src[r])
+            shards[r] = flat[r * S:(r + 1) * S]
+        zs.zs_gather_unit(shards, flat)
+        torch.cuda.synchronize()
+        assert torch.equal(flat, torch.cat(src)), S
