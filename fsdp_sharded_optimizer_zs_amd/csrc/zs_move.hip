@@ -1,22 +1,21 @@
 // Pack (flat unit -> D shards), gather (D shards -> flat unit) and re-shard
 // (D shards -> D' shards of the same unit) for gfx950.
 //
-// Both are bit copies bound by HBM bandwidth. Work is split into runs that
-// are contiguous on both sides (a tensor piece that lands inside one shard,
-// or one shard landing in the flat unit). Lanes write whole 16-byte
+// All three are bit copies bound by HBM bandwidth. Work is split into runs
+// that are contiguous on both sides (a tensor piece that lands inside one
+// shard, or one shard landing in the flat unit). Lanes write whole 16-byte
 // destination vectors (dwordx4 stores); the source is read with dwordx4
 // loads when it is 16-byte aligned relative to the destination and with
 // narrower, still coalesced, loads otherwise; loads and stores of the
 // vector body are non-temporal (each byte is touched once). The few elements
 // before the first and after the last aligned vector of a run are copied one
-// per lane.
-// No lane ever touches a byte outside the run it copies.
+// per lane. No lane ever touches a byte outside the run it copies.
 //
-// Grids cover the work (one lane per 16-byte vector for the gather's copies,
-// one workgroup per 16K-element work item for pack and re-shard) rather than
-// a persistent grid: the hardware then hands out workgroups in order and the
-// open region of HBM stays compact (70B unit gather: 6.21 TB/s against 5.94
-// with a persistent grid of 4 workgroups per CU, same box).
+// Grids cover the work (one lane per 16-byte vector in the gather, one
+// workgroup per 16K-element work item in pack and re-shard) rather than
+// being persistent: the hardware then hands out workgroups in order and the
+// open region of HBM stays compact (70B unit gather per shard: 6.21 TB/s
+// against 5.94 with a persistent grid of 4 workgroups per CU, same box).
 
 #include "zs_internal.h"
 
