@@ -12,7 +12,7 @@
 // per lane. No lane ever touches a byte outside the run it copies.
 //
 // Grids cover the work (one lane per 16-byte vector in the gather, one
-// workgroup per 16K-element work item in pack and re-shard) rather than
+// workgroup per 8 KiB work item in pack and re-shard) rather than
 // being persistent: the hardware then hands out workgroups in order and the
 // open region of HBM stays compact (70B unit gather per shard: 6.21 TB/s
 // against 5.94 with a persistent grid of 4 workgroups per CU, same box).
@@ -25,7 +25,17 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int64_t kPackChunk = 16384;  // flat elements per pack work item
+// Pack and re-shard work items are 8 KiB of destination: 512 aligned 16-byte
+// vectors, two per lane of a 256-thread workgroup, both loads in flight
+// before the stores (kUnroll). Measured on a 70B block unit, one launch over
+// every shard: 8 KiB items 5.9 (pack) and 6.0-6.2 TB/s (re-shard); 16 KiB
+// 5.7 / 5.6-6.2; 4 KiB 4.2-4.7 / 5.2 (the item's table search and index
+// arithmetic are no longer hidden); 64 KiB items launched per shard 5.4.
+constexpr int64_t kItemBytes = 8192;
+constexpr int kUnroll = 2;  // aligned vectors a lane has in flight in copy_run
+
+template <int ES>
+constexpr int64_t kItem = kItemBytes / ES;  // elements per pack / re-shard work item
 
 template <int ES>
 struct Elem;
@@ -60,7 +70,16 @@ __device__ __forceinline__ void copy_run(char* dst, const char* src, int64_t n, 
     const uintptr_t sa = reinterpret_cast<uintptr_t>(sb);
     if ((sa & 15) == 0) {
         const u32x4* s4 = reinterpret_cast<const u32x4*>(sb);
-        for (int64_t i = tid; i < body; i += nthr)
+        int64_t i = tid;
+        // kUnroll loads in flight per lane before their stores
+        for (; i + (kUnroll - 1) * nthr < body; i += kUnroll * nthr) {
+            u32x4 x[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) x[u] = __builtin_nontemporal_load(s4 + i + u * nthr);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(x[u], db + i + u * nthr);
+        }
+        for (; i < body; i += nthr)
             __builtin_nontemporal_store(__builtin_nontemporal_load(s4 + i), db + i);
     } else if ((sa & 3) == 0) {
         const uint32_t* s1 = reinterpret_cast<const uint32_t*>(sb);
@@ -92,8 +111,8 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const zs_tensor_ref* __r
     for (int64_t q = q0 + blockIdx.x; q < q1; q += gridDim.x) {
         const int64_t r = q / per_shard;
         const int64_t base = r * S;
-        const int64_t lo = base + (q - r * per_shard) * kPackChunk;
-        const int64_t hi = lo + kPackChunk < base + S ? lo + kPackChunk : base + S;
+        const int64_t lo = base + (q - r * per_shard) * kItem<ES>;
+        const int64_t hi = lo + kItem<ES> < base + S ? lo + kItem<ES> : base + S;
         char* shard = static_cast<char*>(const_cast<void*>(shards.p[r]));
         // smallest j with flat_offset_j + numel_j > lo
         int a = 0, b = T;
@@ -167,8 +186,8 @@ __global__ __launch_bounds__(kThreads) void reshard_kernel(PtrPack src, int64_t 
     for (int64_t q = q0 + blockIdx.x; q < q1; q += gridDim.x) {
         const int64_t r2 = q / per_shard;
         const int64_t base2 = r2 * S2;
-        const int64_t lo = base2 + (q - r2 * per_shard) * kPackChunk;
-        const int64_t hi = lo + kPackChunk < base2 + S2 ? lo + kPackChunk : base2 + S2;
+        const int64_t lo = base2 + (q - r2 * per_shard) * kItem<ES>;
+        const int64_t hi = lo + kItem<ES> < base2 + S2 ? lo + kItem<ES> : base2 + S2;
         char* d = static_cast<char*>(const_cast<void*>(dst.p[r2]));
         const int64_t real_end = hi < N ? hi : N;
         for (int64_t i = lo; i < real_end;) {
@@ -186,45 +205,46 @@ __global__ __launch_bounds__(kThreads) void reshard_kernel(PtrPack src, int64_t 
 
 }  // namespace
 
-// Pack and re-shard: one launch per destination shard (the work items of
-// shard r are [r * per_shard, (r + 1) * per_shard)), in shard order, for the
-// same reason as the gather's launch per shard.
+namespace {
+
+template <int ES>
+hipError_t reshard_es(const PtrPack& src, int64_t S, const PtrPack& dst, int D2, int64_t S2,
+                      int64_t N, hipStream_t stream) {
+    const int64_t per_shard = (S2 + kItem<ES> - 1) / kItem<ES>;
+    const int64_t items = per_shard * D2;
+    const int64_t blocks = items < 1 ? 1 : (items < kMaxGrid ? items : kMaxGrid);
+    hipLaunchKernelGGL((reshard_kernel<ES>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                       src, S, dst, S2, N, per_shard, int64_t(0), items);
+    return hipGetLastError();
+}
+
+template <int ES>
+hipError_t pack_es(const zs_tensor_ref* d_table, int T, int64_t N, int D, const PtrPack& shards,
+                   int64_t S, hipStream_t stream) {
+    const int64_t per_shard = (S + kItem<ES> - 1) / kItem<ES>;
+    const int64_t items = per_shard * D;
+    const int64_t blocks = items < 1 ? 1 : (items < kMaxGrid ? items : kMaxGrid);
+    hipLaunchKernelGGL((pack_kernel<ES>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                       d_table, T, N, shards, S, per_shard, int64_t(0), items);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Pack and re-shard: one launch over every destination shard, one workgroup
+// per work item (the items of shard r are [r * per_shard, (r + 1) *
+// per_shard)), so that, as in the gather, there is no start and drain per
+// shard.
 hipError_t launch_reshard(const PtrPack& src, int64_t S, const PtrPack& dst, int D2, int64_t S2,
                           int64_t N, int es, hipStream_t stream) {
-    const int64_t per_shard = (S2 + kPackChunk - 1) / kPackChunk;
-    int64_t blocks = per_shard < kMaxGrid ? per_shard : kMaxGrid;
-    if (blocks < 1) blocks = 1;
-    for (int r = 0; r < D2; ++r) {
-        const int64_t q0 = r * per_shard, q1 = q0 + per_shard;
-        if (es == 2)
-            hipLaunchKernelGGL((reshard_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0,
-                               stream, src, S, dst, S2, N, per_shard, q0, q1);
-        else
-            hipLaunchKernelGGL((reshard_kernel<4>), dim3(unsigned(blocks)), dim3(kThreads), 0,
-                               stream, src, S, dst, S2, N, per_shard, q0, q1);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return es == 2 ? reshard_es<2>(src, S, dst, D2, S2, N, stream)
+                   : reshard_es<4>(src, S, dst, D2, S2, N, stream);
 }
 
 hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es, int D,
                        const PtrPack& shards, int64_t S, hipStream_t stream) {
-    const int64_t per_shard = (S + kPackChunk - 1) / kPackChunk;
-    int64_t blocks = per_shard < kMaxGrid ? per_shard : kMaxGrid;
-    if (blocks < 1) blocks = 1;
-    for (int r = 0; r < D; ++r) {
-        const int64_t q0 = r * per_shard, q1 = q0 + per_shard;
-        if (es == 2)
-            hipLaunchKernelGGL((pack_kernel<2>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                               d_table, T, N, shards, S, per_shard, q0, q1);
-        else
-            hipLaunchKernelGGL((pack_kernel<4>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                               d_table, T, N, shards, S, per_shard, q0, q1);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return es == 2 ? pack_es<2>(d_table, T, N, D, shards, S, stream)
+                   : pack_es<4>(d_table, T, N, D, shards, S, stream);
 }
 
 hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es, void* flat,
