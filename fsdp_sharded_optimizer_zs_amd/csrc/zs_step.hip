@@ -161,12 +161,19 @@ __device__ __forceinline__ void fold8(const PtrPack& c, int base, int n, int64_t
         load8<DT>(c.p[base], tile, lane, s);
         if constexpr (NC > 1) add_batch<DT, NC - 1>(c, base + 1, tile, lane, s);
     } else {
-        const int len = NC > 0 ? NC : n;
-        // first batch: c_0 then up to 7 more
-        const int head = len < kBatch ? len : kBatch;
+        // For bf16 the batch loop keeps a run-time trip count (n, which
+        // equals NC when NC is fixed): with the trip count known, the
+        // compiler unrolled the single batch after the first at NC = 16 and
+        // then issued its loads one at a time, each behind a wait for the one
+        // before (16 bf16 contributions: 5.1 TB/s, against 6.2 with the loop
+        // kept). fp32 keeps the fixed count, whose unrolled schedule issues
+        // the first batches of both tiles together (16 fp32 contributions:
+        // 0.7% faster than with the loop kept, same process and buffers).
+        const int len = (DT == ZS_BF16 || NC == 0) ? n : NC;
+        // first batch: c_0 then 7 more when there are at least 8
         load8<DT>(c.p[base], tile, lane, s);
         int q = 1;
-        if (head == kBatch) {
+        if (NC >= kBatch || len >= kBatch) {
             add_batch<DT, kBatch - 1>(c, base + 1, tile, lane, s);
             q = kBatch;
         }

@@ -10,6 +10,10 @@ cross-compiles).
   (16 contribution vectors and 12 state vectors per lane) before it first
   waits on any of them: the schedule that sets its HBM rate. Without the
   kernel's occupancy attribute the compiler interleaves loads and waits.
+- The long bf16 folds (16 and 32 contributions, flat and two-level, fused and
+  reduce-only) issue their contribution loads in batches of 8 before waiting:
+  an unrolled 16-way fold once issued them one at a time behind waits (5.1
+  against 6.2 TB/s).
 """
 import os
 import re
@@ -74,3 +78,30 @@ def test_fused_step_issues_a_tile_pair_of_loads_before_waiting(asm):
         run = run + 1 if op == "global_load_dwordx4" else 0
         longest = max(longest, run)
     assert longest >= 28, f"longest run of loads before a wait: {longest}"
+
+
+def load_runs(body):
+    """Lengths of the runs of dwordx4 loads between two vmcnt waits."""
+    ops = re.findall(r"^\s*(global_load_dwordx4|s_waitcnt\s+vmcnt)", body, re.M)
+    out, run = [], 0
+    for op in ops:
+        if op == "global_load_dwordx4":
+            run += 1
+        else:
+            if run:
+                out.append(run)
+            run = 0
+    if run:
+        out.append(run)
+    return out
+
+
+def test_long_bf16_folds_issue_loads_in_batches(asm):
+    pat = (r"(adamw|reduce)_vec_kernelILi1ENS0_(7FlatSum|9HybridSum)ILi1ELi(16|32)EEELi2E")
+    kern = [(n, b) for n, b in functions(asm["zs_step.hip"]) if re.search(pat, n)]
+    assert len(kern) == 8, [n for n, _ in kern]
+    for n, b in kern:
+        runs = load_runs(b)
+        batched = sum(r for r in runs if r >= 8)
+        # the rest are remainder-loop singles and the fp32 split of a batch
+        assert 3 * batched >= 2 * sum(runs), f"{n}: load runs {runs}"
