@@ -199,14 +199,15 @@ def test_adamw_vs_oracle(code, D):
         run_steps(D, S, code, 3, dev, seed=D)
 
 
-# The tiled kernels take two adjacent 512-element tiles per wavefront and
-# iteration; an odd last tile and the S % 512 tail go to the last workgroup.
-# Sizes around those edges, and one past the persistent grid (the tile-pair
-# loop wraps).
+# The tiled kernels take two adjacent 512-element tiles per wavefront; the
+# elements past the last whole tile pair go to the last workgroup, one per
+# lane. Sizes around those edges, and one of 2,441 tile pairs plus a tail.
+# The long folds (16 and 32 contributions) run their batches of 8 in a loop.
 TILE_EDGE_SIZES = (511, 512, 513, 1024, 1536, 1537, 3 * 1024 + 511, 2_500_517)
 
 
-@pytest.mark.parametrize("code,D", [(zs.ZS_BF16, 8), (zs.ZS_F32, 4), (zs.ZS_BF16, 3)])
+@pytest.mark.parametrize("code,D", [(zs.ZS_BF16, 8), (zs.ZS_F32, 4), (zs.ZS_BF16, 3),
+                                    (zs.ZS_BF16, 16), (zs.ZS_F32, 16), (zs.ZS_BF16, 32)])
 def test_adamw_tile_edges(code, D):
     dev = device()
     for S in TILE_EDGE_SIZES:
