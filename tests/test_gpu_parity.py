@@ -85,6 +85,34 @@ def test_pack_every_source_alignment(dtype):
             check_bits(to_np(flat), O.gather_unit(want), f"gather off={off}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [63, 64, 65, 300, 4097])
+def test_pack_many_tensors(dtype, T):
+    """Long tensor tables (up to 4,097 entries) for the search of each work
+    item's first tensor; a third of the tensors are empty and many hold one
+    element, so that runs of table entries end at the same flat offset, and
+    the sources sit at assorted alignments."""
+    dev = device()
+    rng = np.random.default_rng(T)
+    tdt = torch.int16 if dtype == "bf16" else torch.float32
+    numels = [int(x) for x in rng.choice([0, 0, 1, 3, 17, 700, 5000], size=T)]
+    base = torch.arange(1, sum(numels) + 8 * T + 8, device=dev).to(tdt)
+    ts, pos = [], 0
+    for j, n in enumerate(numels):
+        pos += j % 3                       # sources at assorted alignments
+        ts.append(base[pos:pos + n])
+        pos += n
+    for D in (1, 5, 16):
+        _, N, N_pad, S = zs.zs_unit_layout(numels, D)
+        if S == 0:
+            continue
+        shards = [torch.full((S,), 77, dtype=tdt, device=dev) for _ in range(D)]
+        zs.zs_pack_flat(ts, D, shards)
+        want = O.pack_flat([to_np(t) for t in ts], D)
+        for r in range(D):
+            check_bits(to_np(shards[r]), want[r], f"T={T} D={D} shard {r}")
+
+
 def test_pack_gpt3m_unit():
     """The 3.3M-parameter GPT unit (43 tensors), fp32 and bf16, D = 4."""
     dev = device()
