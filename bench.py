@@ -481,9 +481,6 @@ def main() -> int:
     ap.add_argument("--no-copy", action="store_true",
                     help="skip the plain 4 GiB device copy (the copy ceiling and the HBM "
                          "counter calibration)")
-    ap.add_argument("--copy-calibrate", action="store_true",
-                    help="no effect: the copy runs unless --no-copy (accepted so that the "
-                         "recorded counter commands still run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the shard step is measured on one GPU only (asked for --gpus {args.gpus}); the "

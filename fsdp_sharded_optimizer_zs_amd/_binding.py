@@ -138,13 +138,17 @@ def _torch():
     return torch
 
 
-def _dtype_code(t) -> int:
+def _dtype_code_of(dtype) -> int:
     torch = _torch()
-    if t.dtype in (torch.bfloat16, torch.int16) or t.dtype == getattr(torch, "uint16", None):
+    if dtype in (torch.bfloat16, torch.int16) or dtype == getattr(torch, "uint16", None):
         return ZS_BF16
-    if t.dtype == torch.float32:
+    if dtype == torch.float32:
         return ZS_F32
-    raise TypeError(f"unsupported dtype {t.dtype}: use bf16 (bfloat16/int16 bits) or float32")
+    raise TypeError(f"unsupported dtype {dtype}: use bf16 (bfloat16/int16 bits) or float32")
+
+
+def _dtype_code(t) -> int:
+    return _dtype_code_of(t.dtype)
 
 
 def _dev(t, what: str):
@@ -193,26 +197,37 @@ def zs_pack_flat(tensors: Sequence, D: int, shards: Sequence, stream=None):
     shard tensors of S elements each. Returns the device tensor table, which
     the enqueued kernel reads (stream-ordered; keep it or let torch's
     caching allocator recycle it on the same stream)."""
+    import numpy as np
     torch = _torch()
     if len(shards) != D:
         raise ValueError("need exactly D shard tensors")
     ref = shards[0]
     code = _dtype_code(ref)
-    for i, t in enumerate(list(tensors) + list(shards)):
-        _dev(t, f"tensor {i}")
-        if _dtype_code(t) != code or t.element_size() != ref.element_size():
-            raise TypeError("tensors and shards must share one element type")
-    offsets, N, _, S = zs_unit_layout([t.numel() for t in tensors], D)
+    tensors = list(tensors)
+    everything = tensors + list(shards)
+    # one pass per property, then the failing index for the message
+    same = {t.dtype for t in everything}
+    if not all(t.is_cuda and t.is_contiguous() for t in everything) or any(
+            _dtype_code_of(d) != code for d in same) or len(
+            {t.element_size() for t in everything}) != 1:
+        for i, t in enumerate(everything):
+            _dev(t, f"tensor {i}")
+            if _dtype_code(t) != code or t.element_size() != ref.element_size():
+                raise TypeError("tensors and shards must share one element type")
+    T = len(tensors)
+    numels = [t.numel() for t in tensors]
+    offsets, N, _, S = zs_unit_layout(numels, D)
     if any(s.numel() != S for s in shards):
         raise ValueError(f"every shard must hold S = {S} elements")
-    T = len(tensors)
-    h = (zs_tensor_ref * max(1, T))()
-    rows = []
-    for j, t in enumerate(tensors):
-        h[j] = zs_tensor_ref(t.data_ptr(), t.numel(), offsets[j])
-        rows.append((t.data_ptr(), t.numel(), offsets[j]))
-    d_table = (torch.tensor(rows, dtype=torch.int64) if rows
-               else torch.zeros((0, 3), dtype=torch.int64)).to(ref.device)
+    # the table rows are zs_tensor_ref: (ptr, numel, flat_offset), 3 x 8 bytes
+    tab = np.empty((max(1, T), 3), dtype=np.int64)
+    if T:
+        tab[:T, 0] = np.array([t.data_ptr() for t in tensors], dtype=np.uint64).view(np.int64)
+        tab[:T, 1] = numels
+        tab[:T, 2] = offsets[:T]
+    h = tab.ctypes.data_as(ctypes.POINTER(zs_tensor_ref))
+    d_table = (torch.from_numpy(tab[:T]).to(ref.device) if T
+               else torch.zeros((0, 3), dtype=torch.int64, device=ref.device))
     if isinstance(stream, torch.cuda.Stream):
         # the kernel reads the table on `stream`: tell the caching allocator
         d_table.record_stream(stream)
