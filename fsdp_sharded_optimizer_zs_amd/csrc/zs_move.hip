@@ -5,9 +5,9 @@
 // that are contiguous on both sides (a tensor piece that lands inside one
 // shard, or one shard landing in the flat unit). Lanes write whole 16-byte
 // destination vectors (dwordx4 stores); the source is read with dwordx4
-// loads when it is 16-byte aligned relative to the destination and with
-// narrower, still coalesced, loads otherwise; loads and stores of the
-// vector body are non-temporal (each byte is touched once). The few elements
+// loads when it is at least 4-byte aligned and with 2-byte loads when bf16
+// sits at an odd element offset (all still coalesced); loads and stores of
+// the vector body are non-temporal (each byte is touched once). The few elements
 // before the first and after the last aligned vector of a run are copied one
 // per lane. No lane ever touches a byte outside the run it copies.
 //
