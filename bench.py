@@ -214,38 +214,45 @@ def hybrid_leg(zs, torch, W, dev, hp, steps: int, arenas):
 
 def hbm_directions(zs, torch, dev, read_bytes: int, write_bytes: int):
     """HBM's own rates for one direction at a time (zs_hbm_probe: reads,
-    writes and a copy over a 4 GiB buffer, the best of a grid that covers the
-    buffer and persistent grids of 1-4 workgroups per CU)
+    writes and a copy over a 4 GiB buffer, and a triad of two 4 GiB read
+    streams and one write stream -- the step's 2:1 ratio in three streams --,
+    the best of a grid that covers the buffers and persistent grids of 1-4
+    workgroups per CU)
     and the rate the step's mix of read_bytes and write_bytes per param would
     reach if reads and writes overlapped perfectly at those rates."""
     n = 4 << 30
-    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    a2 = torch.empty(2 * n, dtype=torch.uint8, device=dev)   # the triad's two read streams
+    a = a2[:n]
     b = torch.empty(n, dtype=torch.uint8, device=dev)
-    zs.zs_hbm_probe(zs.ZS_PROBE_WRITE, a)
+    zs.zs_hbm_probe(zs.ZS_PROBE_WRITE, a2)
     torch.cuda.synchronize()
     best = {}
     for name, kind, moved in (("read", zs.ZS_PROBE_READ, n), ("write", zs.ZS_PROBE_WRITE, n),
-                              ("copy", zs.ZS_PROBE_COPY, 2 * n)):
+                              ("copy", zs.ZS_PROBE_COPY, 2 * n),
+                              ("triad", zs.ZS_PROBE_TRIAD, 3 * n)):
         for per_cu in (0, 1, 2, 3, 4):
-            dst = b[:16] if kind == zs.ZS_PROBE_READ else (b if kind == zs.ZS_PROBE_COPY else None)
+            dst = b[:16] if kind == zs.ZS_PROBE_READ else (None if kind == zs.ZS_PROBE_WRITE
+                                                           else b)
+            src = a2 if kind == zs.ZS_PROBE_TRIAD else a
             ms = []
             for _ in range(3):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                zs.zs_hbm_probe(kind, a, dst, blocks_per_cu=per_cu)
+                zs.zs_hbm_probe(kind, src, dst, blocks_per_cu=per_cu)
                 e1.record()
                 torch.cuda.synchronize()
                 ms.append(e0.elapsed_time(e1))
             rate = moved / (min(ms) / 1e3) / 1e9
             if rate > best.get(name, (0.0, 0))[0]:
                 best[name] = (rate, per_cu)
-    del a, b
+    del a, a2, b
     torch.cuda.empty_cache()
     rd, wr = best["read"][0], best["write"][0]
     bound = (read_bytes + write_bytes) / (read_bytes / rd + write_bytes / wr)
     return {"read_GB_s": rd, "read_blocks_per_cu": best["read"][1],
             "write_GB_s": wr, "write_blocks_per_cu": best["write"][1],
             "copy_GB_s": best["copy"][0], "copy_blocks_per_cu": best["copy"][1],
+            "triad_GB_s": best["triad"][0], "triad_blocks_per_cu": best["triad"][1],
             "step_mix": f"{read_bytes} B read + {write_bytes} B written per param",
             "ideal_overlap_bound_GB_s": bound}
 
@@ -668,6 +675,7 @@ def main() -> int:
         log("HBM direction probes: reads, writes and a copy alone")
         dirs = hbm_directions(zs, torch, dev, read_bytes=28, write_bytes=14)
         dirs["fused_over_bound"] = achieved / dirs["ideal_overlap_bound_GB_s"]
+        dirs["fused_over_triad"] = achieved / dirs["triad_GB_s"]
         out["roofline"]["hbm_directions"] = dirs
     if not args.no_copy:
         a = torch.empty(1 << 30, device=dev)          # 4 GiB fp32

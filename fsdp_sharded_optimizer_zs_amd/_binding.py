@@ -521,23 +521,28 @@ def zs_stream_ceiling(p, m, v, w, contribs: Sequence, stream=None) -> None:
                                     _stream(p, stream)))
 
 
-ZS_PROBE_READ, ZS_PROBE_WRITE, ZS_PROBE_COPY = 0, 1, 2
+ZS_PROBE_READ, ZS_PROBE_WRITE, ZS_PROBE_COPY, ZS_PROBE_TRIAD = 0, 1, 2, 3
 
 
 def zs_hbm_probe(kind: int, buf, buf2=None, blocks_per_cu: int = 1, stream=None) -> None:
     """Measurement aid: read, write or copy all of buf (any dtype; its byte
-    size a multiple of 16) with the library's streaming access pattern.
-    buf2: the copy's destination (at least as large as buf), or a 16-byte
-    sink for a read."""
+    size a multiple of 16) with the library's streaming access pattern, or a
+    triad: buf2 = first half of buf XOR second half (buf's byte size a
+    multiple of 32). buf2: the copy's or triad's destination (at least as
+    large as what it receives), or a 16-byte sink for a read."""
     _dev(buf, "buf")
     nbytes = buf.numel() * buf.element_size()
+    if kind == ZS_PROBE_TRIAD:
+        if nbytes % 32:
+            raise ValueError("a triad's buf must hold a multiple of 32 bytes")
+        nbytes //= 2
     if buf2 is not None:
         _dev(buf2, "buf2")
-        need = nbytes if kind == ZS_PROBE_COPY else 16
+        need = 16 if kind == ZS_PROBE_READ else nbytes
         if buf2.numel() * buf2.element_size() < need:
             raise ValueError(f"buf2 must hold at least {need} bytes")
     elif kind != ZS_PROBE_WRITE:
-        raise ValueError("buf2 is required for read and copy")
+        raise ValueError("buf2 is required for read, copy and triad")
     _check(load().zs_hbm_probe(int(kind), buf.data_ptr(),
                                buf2.data_ptr() if buf2 is not None else None, nbytes,
                                int(blocks_per_cu), _stream(buf, stream)))

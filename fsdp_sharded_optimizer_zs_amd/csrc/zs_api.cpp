@@ -133,7 +133,7 @@ using namespace zs;
 
 ZS_EXPORT const char* zs_last_error(void) { return g_last_error.c_str(); }
 
-ZS_EXPORT int32_t zs_abi_version(void) { return 106; }
+ZS_EXPORT int32_t zs_abi_version(void) { return 107; }
 
 ZS_EXPORT zs_status zs_unit_layout(const int64_t* numels, int32_t T, int32_t D,
                                    int64_t* offsets_out, int64_t* n_out, int64_t* n_pad_out,
@@ -422,11 +422,12 @@ ZS_EXPORT zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w,
 ZS_EXPORT zs_status zs_hbm_probe(int32_t kind, void* buf, void* buf2, int64_t bytes,
                                  int32_t blocks_per_cu, hipStream_t stream) {
     const char* who = "zs_hbm_probe";
-    if (kind != ZS_PROBE_READ && kind != ZS_PROBE_WRITE && kind != ZS_PROBE_COPY)
+    if (kind != ZS_PROBE_READ && kind != ZS_PROBE_WRITE && kind != ZS_PROBE_COPY &&
+        kind != ZS_PROBE_TRIAD)
         return fail(ZS_EINVAL, "%s: unknown kind %d", who, kind);
     if (blocks_per_cu < 0 || blocks_per_cu > 16)
         return fail(ZS_EINVAL, "%s: blocks_per_cu = %d outside 0..16", who, blocks_per_cu);
-    if (bytes < 0 || bytes % 16 != 0 || !size_ok(bytes / 16, 16))
+    if (bytes < 0 || bytes % 16 != 0 || !size_ok(bytes / 16, 32))
         return fail(ZS_EINVAL, "%s: bytes = %lld is not a non-negative multiple of 16", who,
                     (long long)bytes);
     if (bytes == 0) return ok();
@@ -436,8 +437,9 @@ ZS_EXPORT zs_status zs_hbm_probe(int32_t kind, void* buf, void* buf2, int64_t by
     if (two) {
         if (buf2 == nullptr || !aligned(buf2, 16))
             return fail(ZS_EINVAL, "%s: buf2 is NULL or not 16-byte aligned", who);
-        const int64_t n2 = kind == ZS_PROBE_COPY ? bytes : 16;
-        if (overlap(range_of(buf, bytes, 1), range_of(buf2, n2, 1)))
+        const int64_t n1 = kind == ZS_PROBE_TRIAD ? 2 * bytes : bytes;
+        const int64_t n2 = kind == ZS_PROBE_READ ? 16 : bytes;
+        if (overlap(range_of(buf, n1, 1), range_of(buf2, n2, 1)))
             return fail(ZS_EALIAS, "%s: buf and buf2 overlap", who);
     }
     return hip_status(launch_probe(kind, buf, buf2, bytes / 16, blocks_per_cu, stream), who);

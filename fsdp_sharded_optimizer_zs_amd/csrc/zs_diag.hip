@@ -110,10 +110,11 @@ streams_kernel(float* __restrict__ p, float* __restrict__ m, float* __restrict__
         tiles<BF16, kPair>(p4, m4, v4, w2, c, n, q * kPair, lane, xpose[wave]);
 }
 
-// Single-direction and copy streams over one buffer, for the memory system's
-// own rates: reads (two 16-byte vectors per lane in flight), writes (one
-// 16-byte vector per lane) and a copy, all non-temporal, in the grid-stride
-// order of the step kernels. nvec counts 16-byte vectors.
+// Single-direction, copy and triad streams, for the memory system's own
+// rates: reads (two 16-byte vectors per lane in flight), writes (one 16-byte
+// vector per lane), a copy and a triad (two reads per write), all
+// non-temporal, in the grid-stride order of the step kernels. nvec counts
+// 16-byte vectors per stream.
 __global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4* __restrict__ a,
                                                               int64_t nvec,
                                                               u32x4* __restrict__ sink) {
@@ -143,6 +144,19 @@ __global__ __launch_bounds__(kThreads) void probe_copy_kernel(const u32x4* __res
     const int64_t stride = int64_t(gridDim.x) * kThreads;
     for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride)
         __builtin_nontemporal_store(__builtin_nontemporal_load(a + i), b + i);
+}
+
+// Two read streams for each write stream, the fused step's ratio in three
+// streams: c[i] = a0[i] ^ a1[i], a0 = a[0, nvec), a1 = a[nvec, 2 nvec).
+__global__ __launch_bounds__(kThreads) void probe_triad_kernel(const u32x4* __restrict__ a,
+                                                               u32x4* __restrict__ c,
+                                                               int64_t nvec) {
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride) {
+        const u32x4 x = __builtin_nontemporal_load(a + i);
+        const u32x4 y = __builtin_nontemporal_load(a + nvec + i);
+        __builtin_nontemporal_store(x ^ y, c + i);
+    }
 }
 
 }  // namespace
@@ -178,6 +192,8 @@ hipError_t launch_probe(int kind, void* buf, void* buf2, int64_t nvec, int per_c
         hipLaunchKernelGGL(probe_read_kernel, grid, block, 0, stream, a, nvec, b);
     else if (kind == ZS_PROBE_WRITE)
         hipLaunchKernelGGL(probe_write_kernel, grid, block, 0, stream, a, nvec);
+    else if (kind == ZS_PROBE_TRIAD)
+        hipLaunchKernelGGL(probe_triad_kernel, grid, block, 0, stream, a, b, nvec);
     else
         hipLaunchKernelGGL(probe_copy_kernel, grid, block, 0, stream, a, b, nvec);
     return hipGetLastError();

@@ -466,9 +466,9 @@ zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w, int64_t S
 
 /*
  * zs_hbm_probe -- a measurement aid, not part of the step: the memory
- * system's own rate for one stream direction, so that the step kernel's mix
- * of reads and writes can be read against what HBM gives each direction
- * alone. Non-temporal 16-byte vector accesses in grid-stride order, on a
+ * system's own rate for one stream direction, a copy or a triad, so that the
+ * step kernel's mix of reads and writes can be read against what HBM gives
+ * each direction alone and a plain mix with the same ratio. Non-temporal 16-byte vector accesses in grid-stride order, on a
  * grid of 256-thread workgroups that covers the buffer (blocks_per_cu = 0)
  * or on a persistent grid of blocks_per_cu workgroups per CU:
  *
@@ -477,14 +477,17 @@ zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w, int64_t S
  *   ZS_PROBE_WRITE  writes bytes of buf (element i of each 16-byte vector v:
  *                   {v mod 2^32, v >> 32, 0x5a5a5a5a, 0} as uint32 words)
  *   ZS_PROBE_COPY   copies bytes of buf to buf2
+ *   ZS_PROBE_TRIAD  two reads per write, the fused step's ratio in three
+ *                   streams: buf holds 2 * bytes, buf2[i] = buf[i] ^
+ *                   buf[bytes + i] for the bytes of buf2 (XOR of 32-bit words)
  *
- *   bytes           a multiple of 16; 0 returns ZS_OK with no launch
+ *   bytes           a multiple of 16 (per stream); 0 returns ZS_OK with no launch
  *   buf, buf2       16-byte aligned device pointers; buf2 unused for WRITE;
- *                   for READ and COPY buf2 must not overlap buf
+ *                   for READ, COPY and TRIAD buf2 must not overlap buf
  *   blocks_per_cu   0..16
  * Errors: ZS_EINVAL (kind, sizes, alignment, NULL), ZS_EALIAS, ZS_EHIP.
  */
-enum { ZS_PROBE_READ = 0, ZS_PROBE_WRITE = 1, ZS_PROBE_COPY = 2 };
+enum { ZS_PROBE_READ = 0, ZS_PROBE_WRITE = 1, ZS_PROBE_COPY = 2, ZS_PROBE_TRIAD = 3 };
 zs_status zs_hbm_probe(int32_t kind, void* buf, void* buf2, int64_t bytes,
                        int32_t blocks_per_cu, hipStream_t stream);
 

@@ -373,7 +373,7 @@ def test_shard_save_and_load_argument_errors(lib, tmp_path):
 
 def test_hbm_probe_argument_errors(lib):
     probe = lib.zs_hbm_probe
-    assert probe(3, A, A + (1 << 20), 1 << 20, 1, None) == zs.ZS_EINVAL          # kind
+    assert probe(4, A, A + (1 << 22), 1 << 20, 1, None) == zs.ZS_EINVAL          # kind
     assert probe(zs.ZS_PROBE_READ, A, A + (1 << 20), 1 << 20, -1, None) == zs.ZS_EINVAL
     assert probe(zs.ZS_PROBE_READ, A, A + (1 << 20), 1 << 20, 17, None) == zs.ZS_EINVAL
     assert probe(zs.ZS_PROBE_WRITE, A, None, 100, 1, None) == zs.ZS_EINVAL        # not 16k
@@ -381,6 +381,9 @@ def test_hbm_probe_argument_errors(lib):
     assert probe(zs.ZS_PROBE_WRITE, None, None, 1 << 20, 1, None) == zs.ZS_EINVAL
     assert probe(zs.ZS_PROBE_WRITE, A + 8, None, 1 << 20, 1, None) == zs.ZS_EINVAL
     assert probe(zs.ZS_PROBE_COPY, A, None, 1 << 20, 1, None) == zs.ZS_EINVAL
+    assert probe(zs.ZS_PROBE_TRIAD, A, None, 1 << 20, 1, None) == zs.ZS_EINVAL
+    # the triad reads 2 * bytes of buf: a destination inside its second half overlaps
+    assert probe(zs.ZS_PROBE_TRIAD, A, A + (1 << 20) + 4096, 1 << 20, 1, None) == zs.ZS_EALIAS
     assert probe(zs.ZS_PROBE_COPY, A, A + 4, 1 << 20, 1, None) == zs.ZS_EINVAL     # misaligned
     assert probe(zs.ZS_PROBE_COPY, A, A + 4096, 1 << 20, 1, None) == zs.ZS_EALIAS
     assert "overlap" in zs.zs_last_error()

@@ -88,3 +88,10 @@ def test_hbm_probe_write_copy_read(per_cu):
     zs.zs_hbm_probe(zs.ZS_PROBE_READ, src, sink, blocks_per_cu=per_cu)
     torch.cuda.synchronize()
     assert torch.equal(src, before)
+
+    two = torch.randint(0, 256, (2 * n,), dtype=torch.uint8, device=dev)
+    out = torch.zeros(n + guard, dtype=torch.uint8, device=dev)
+    zs.zs_hbm_probe(zs.ZS_PROBE_TRIAD, two, out[:n], blocks_per_cu=per_cu)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor(to_np(two[:n]), to_np(two[n:]))
+    assert np.array_equal(to_np(out[:n]), want) and not to_np(out[n:]).any()
