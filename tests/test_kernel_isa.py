@@ -10,10 +10,10 @@ cross-compiles).
   (16 contribution vectors and 12 state vectors per lane) before it first
   waits on any of them: the schedule that sets its HBM rate. Without the
   kernel's occupancy attribute the compiler interleaves loads and waits.
-- The long bf16 folds (16 and 32 contributions, flat and two-level, fused and
-  reduce-only) issue their contribution loads in batches of 8 before waiting:
-  an unrolled 16-way fold once issued them one at a time behind waits (5.1
-  against 6.2 TB/s).
+- The long bf16 folds (16 and 32 contributions and run-time group sizes, flat
+  and two-level, fused and reduce-only) issue their contribution loads in
+  batches before waiting: an unrolled 16-way fold once issued them one at a
+  time behind waits (5.1 against 6.2 TB/s).
 """
 import os
 import re
@@ -97,11 +97,14 @@ def load_runs(body):
 
 
 def test_long_bf16_folds_issue_loads_in_batches(asm):
-    pat = (r"(adamw|reduce)_vec_kernelILi1ENS0_(7FlatSum|9HybridSum)ILi1ELi(16|32)EEELi2E")
+    # flat and two-level, fused and reduce-only, at 16 and 32 contributions
+    # and at run-time group sizes (a loop of batches of 8, then one batch of
+    # the remainder): loads issued one at a time behind a wait stay rare
+    # (the unrolled 16-way fold that was 5.1 TB/s had 28 of its 44 such)
+    pat = (r"(adamw|reduce)_vec_kernelILi1ENS0_(7FlatSum|9HybridSum)ILi1ELi(0|16|32)EEELi2E")
     kern = [(n, b) for n, b in functions(asm["zs_step.hip"]) if re.search(pat, n)]
-    assert len(kern) == 8, [n for n, _ in kern]
+    assert len(kern) == 12, [n for n, _ in kern]
     for n, b in kern:
         runs = load_runs(b)
-        batched = sum(r for r in runs if r >= 8)
-        # the rest are remainder-loop singles and the fp32 split of a batch
-        assert 3 * batched >= 2 * sum(runs), f"{n}: load runs {runs}"
+        singles = sum(1 for r in runs if r == 1)
+        assert 10 * singles <= sum(runs), f"{n}: load runs {runs}"
