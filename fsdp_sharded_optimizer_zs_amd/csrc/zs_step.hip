@@ -178,18 +178,16 @@ __device__ __forceinline__ void fold8(const PtrPack& c, int base, int n, int64_t
         // the first batches of both tiles together (16 fp32 contributions:
         // 0.7% faster than with the loop kept, same process and buffers).
         const int len = (DT == ZS_BF16 || NC == 0) ? n : NC;
-        // For bf16 the first batch (up to 8) and the remainder after the
-        // whole batches (up to 7) go out as one batch each, through a switch
-        // over the batch sizes; one load at a time ran n = 3, 5, 7 and 13
-        // 6-14% slower (5.3-5.7 against 6.0 TB/s). fp32 keeps single loads
-        // for the remainder, which measured 0.8% faster at n = 12.
+        // The first batch (up to 8) goes out as one batch through a switch
+        // over the batch sizes, and for bf16 so does the remainder after the
+        // whole batches (up to 7); one load at a time ran bf16 n = 3, 5, 7
+        // and 13 6-14% slower (5.3-5.7 against 6.0 TB/s) and fp32 n = 3, 5,
+        // 7 1-4% slower. fp32 keeps single loads for the remainder, which
+        // measured 0.8% faster at n = 12.
         int q;
         if (NC >= kBatch || len >= kBatch) {
             first_batch<DT, kBatch>(c, base, tile, lane, s);
             q = kBatch;
-        } else if constexpr (DT != ZS_BF16) {
-            first_batch<DT, 1>(c, base, tile, lane, s);
-            q = 1;
         } else {
             switch (len) {
                 case 7: first_batch<DT, 7>(c, base, tile, lane, s); break;
