@@ -123,3 +123,61 @@ def test_host_working_shard_rounding_all_fp32_patterns():
         assert bad.size == 0, f"{bad.size} patterns differ near {a:#x}, first {bits[bad[0]]:#010x}"
         assert (((got[nan] & 0x7FFF) > 0x7F80) & ((got[nan] >> 15) == (bits[nan] >> 31))).all()
         assert np.array_equal(p.numpy().view(np.uint32)[~nan], bits[~nan])
+
+
+def test_concurrent_callers_share_the_worker_pool():
+    """Several host threads call the host step at once (ctypes drops the
+    GIL for the call), each on its own state with its own hyperparameters,
+    while other threads make calls that fail with their own messages: every
+    result equals the oracle's and every thread reads only its own error."""
+    import ctypes
+    import threading
+    lib = zs.load()
+    i64 = ctypes.c_int64
+    n_step, n_err, rounds = 6, 4, 5
+    results, errors = {}, []
+
+    def stepper(j):
+        try:
+            S = 200_003 + 977 * j
+            p, m, v, w = host_state(S, 50 + j)
+            op, om, ov = p.numpy().copy(), m.numpy().copy(), v.numpy().copy()
+            for t in range(1, rounds + 1):
+                g = grads(S, 1000 * j + t)
+                hp = dict(HP, lr=HP["lr"] * (1 + j), step=t)
+                zs.zs_adamw_step_host(p, m, v, w, g, hp, threads=1 + j % 4)
+                op, om, ov, ow = O.adamw_step(op, om, ov, g.numpy(), O.AdamWHP(**hp))
+            results[j] = (p.numpy(), m.numpy(), v.numpy(), w.numpy().view(np.uint16),
+                          op, om, ov, ow)
+        except Exception as e:  # reported below, on the main thread
+            errors.append(f"stepper {j}: {e!r}")
+
+    def failer(j):
+        try:
+            for _ in range(200):
+                # D outside 1..ZS_MAX_D: the message names this thread's D
+                D = 1000 + j
+                numels = (i64 * 1)(5)
+                off = (i64 * 2)()
+                a, b, c = i64(), i64(), i64()
+                st = lib.zs_unit_layout(numels, 1, D, off, a, b, c)
+                msg = lib.zs_last_error().decode()
+                if st != zs.ZS_EINVAL or f"D = {D}" not in msg:
+                    errors.append(f"failer {j}: status {st}, message {msg!r}")
+                    return
+        except Exception as e:
+            errors.append(f"failer {j}: {e!r}")
+
+    ths = [threading.Thread(target=stepper, args=(j,)) for j in range(n_step)]
+    ths += [threading.Thread(target=failer, args=(j,)) for j in range(n_err)]
+    for th in ths:
+        th.start()
+    for th in ths:
+        th.join()
+    assert not errors, errors
+    assert sorted(results) == list(range(n_step))
+    for j, (p, m, v, w, op, om, ov, ow) in results.items():
+        check(p, op, f"thread {j} p")
+        check(m, om, f"thread {j} m")
+        check(v, ov, f"thread {j} v")
+        check(w, ow, f"thread {j} w")
