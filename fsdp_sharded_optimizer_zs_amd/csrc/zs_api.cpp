@@ -87,15 +87,28 @@ zs_status check_hp(const zs_adamw_hp* hp, const char* who) {
 }
 
 AdamConsts adam_consts(const zs_adamw_hp& hp, int n_contrib) {
-    // Double arithmetic, each constant rounded to fp32 once.
-    double b1t = 1.0, b2t = 1.0;
-    for (int64_t t = 0; t < hp.step; ++t) {
-        b1t = b1t * hp.beta1;
-        b2t = b2t * hp.beta2;
-        // Below 2^-54, 1 - b rounds to exactly 1.0 in double, so more
-        // factors cannot change any constant derived from b1t or b2t.
-        if (b1t < 0x1p-54 && b2t < 0x1p-54) break;
+    // Double arithmetic, each constant rounded to fp32 once. beta^t is t
+    // successive multiplications from 1.0. A training run asks for t, t + 1,
+    // ... with the same betas, and every bucket of a step for the same t, so
+    // the powers this thread computed last are kept and advanced from (the
+    // same products, at O(1) per call instead of O(t)); a change of betas or
+    // an earlier t starts again from 1.0.
+    struct Powers {
+        double beta1, beta2;
+        int64_t t;  // b1t = beta1^t, b2t = beta2^t
+        double b1t, b2t;
+    };
+    thread_local Powers pw{-1.0, -1.0, 0, 1.0, 1.0};
+    if (pw.beta1 != hp.beta1 || pw.beta2 != hp.beta2 || pw.t > hp.step)
+        pw = Powers{hp.beta1, hp.beta2, 0, 1.0, 1.0};
+    // Below 2^-54, 1 - b rounds to exactly 1.0 in double, so more factors
+    // cannot change any constant derived from b1t or b2t: stop there.
+    while (pw.t < hp.step && !(pw.b1t < 0x1p-54 && pw.b2t < 0x1p-54)) {
+        pw.b1t = pw.b1t * hp.beta1;
+        pw.b2t = pw.b2t * hp.beta2;
+        ++pw.t;
     }
+    const double b1t = pw.b1t, b2t = pw.b2t;
     AdamConsts k;
     k.dec = float(1.0 - hp.lr * hp.weight_decay);
     k.b1 = float(hp.beta1);

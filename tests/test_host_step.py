@@ -181,3 +181,27 @@ def test_concurrent_callers_share_the_worker_pool():
         check(m, om, f"thread {j} m")
         check(v, ov, f"thread {j} v")
         check(w, ow, f"thread {j} w")
+
+
+def test_step_constants_over_sequences_of_step_counts():
+    """The library keeps the beta powers it computed last on each thread and
+    advances from them; every order of step counts (forward, repeated, back
+    to an earlier step, large, with other betas in between) gives the
+    oracle's constants: the host step's results are the oracle's bit for
+    bit."""
+    S = 4099
+    seq = [(1, HP), (2, HP), (2, HP), (200_000, HP), (200_001, HP), (5, HP),
+           (5, dict(HP, beta2=0.99999)), (70_000, dict(HP, beta2=0.99999)),
+           (70_000, HP), (3, dict(HP, beta1=0.0, beta2=0.0)), (4, dict(HP, beta1=0.0, beta2=0.0)),
+           (123_456, HP)]
+    for i, (t, hpd) in enumerate(seq):
+        p, m, v, w = host_state(S, 300 + i)
+        m.copy_(grads(S, 400 + i)); v.copy_(grads(S, 500 + i).square())
+        g = grads(S, 600 + i)
+        op, om, ov = p.numpy().copy(), m.numpy().copy(), v.numpy().copy()
+        hp = dict(hpd, step=t)
+        zs.zs_adamw_step_host(p, m, v, w, g, hp, threads=2)
+        op, om, ov, ow = O.adamw_step(op, om, ov, g.numpy(), O.AdamWHP(**hp))
+        check(p.numpy(), op, f"p at {i}: step {t}")
+        check(v.numpy(), ov, f"v at {i}: step {t}")
+        check(w.numpy().view(np.uint16), ow, f"w at {i}: step {t}")
