@@ -425,3 +425,41 @@ def test_gather_in_place_d64_last_shard():
         zs.zs_gather_unit(shards, flat)
         torch.cuda.synchronize()
         assert torch.equal(flat, torch.cat(src)), S
+
+
+def test_native_bfloat16_tensors():
+    """Callers may pass torch.bfloat16 tensors wherever bf16 bits are taken
+    (tensors to pack, shards, contributions, the working shard, the unit
+    buffer): the results are the bits of the int16 path and the oracle's."""
+    dev = device()
+    D, numels = 4, [300, 4097, 1, 2048]
+    ts = [W.normal_f32(n, 0.02, 70 + j, dev).to(torch.bfloat16) for j, n in enumerate(numels)]
+    _, N, N_pad, S = zs.zs_unit_layout(numels, D)
+    sh_b = [torch.empty(S, dtype=torch.bfloat16, device=dev) for _ in range(D)]
+    sh_i = [torch.empty(S, dtype=torch.int16, device=dev) for _ in range(D)]
+    zs.zs_pack_flat(ts, D, sh_b)
+    zs.zs_pack_flat([t.view(torch.int16) for t in ts], D, sh_i)
+    want = O.pack_flat([to_np(t) for t in ts], D)
+    for r in range(D):
+        check_bits(to_np(sh_b[r]), want[r], f"bfloat16 shard {r}")
+        check_bits(to_np(sh_i[r]), want[r], f"int16 shard {r}")
+    # fused step: bfloat16 contributions and working shard
+    cs = [W.normal_f32(S, W.GRAD_SCALE, 90 + k, dev).to(torch.bfloat16) for k in range(D)]
+    p0 = W.master_init(S, 11, dev)
+    pb, mb, vb = p0.clone(), torch.zeros(S, device=dev), torch.zeros(S, device=dev)
+    pi, mi, vi = p0.clone(), torch.zeros(S, device=dev), torch.zeros(S, device=dev)
+    wb = torch.empty(S, dtype=torch.bfloat16, device=dev)
+    wi = torch.empty(S, dtype=torch.int16, device=dev)
+    hp = zs.AdamWHP(step=1, **HP)
+    zs.zs_adamw_step(pb, mb, vb, wb, cs, hp)
+    zs.zs_adamw_step(pi, mi, vi, wi, [c.view(torch.int16) for c in cs], hp)
+    op, om, ov, ow = O.rank_step(to_np(p0), np.zeros(S, np.float32), np.zeros(S, np.float32),
+                                 [to_np(c) for c in cs], O.BF16, O.AdamWHP(step=1, **HP))
+    for got, what in ((pb, "p"), (pi, "p int16")):
+        check_f32(to_np(got), op, what, exact=True)
+    check_bf16(to_np(wb), ow, "w bfloat16", exact=True)
+    check_bf16(to_np(wi), ow, "w int16", exact=True)
+    # gather into a bfloat16 unit buffer
+    flat = torch.empty(D * S, dtype=torch.bfloat16, device=dev)
+    zs.zs_gather_unit(sh_b, flat)
+    check_bits(to_np(flat), O.gather_unit(want), "bfloat16 unit")
