@@ -32,15 +32,17 @@ def test_round_trip_every_bf16_pattern():
 
 @pytest.mark.slow
 def test_round_every_fp32_pattern():
-    """All 2^32 fp32 bit patterns, in chunks; NaNs compared by class only."""
-    step = 1 << 26
+    """All 2^32 fp32 bit patterns, in chunks; NaNs compared by class only.
+    Chunks of 2^21 keep every temporary below the allocator's mmap threshold,
+    so memory is reused instead of faulted in afresh (4-5x faster than 2^26)."""
+    step = 1 << 21
     for start in range(0, 1 << 32, step):
-        u = np.arange(start, start + step, dtype=np.uint64).astype(np.uint32)
+        u = np.arange(start, start + step, dtype=np.uint32)
         x = u.view(np.float32)
         a = O.bf16_round(x)
         b = torch_round(x)
         nan = (u & 0x7FFFFFFF) > 0x7F800000
-        assert np.array_equal(a[~nan], b[~nan]), hex(start)
+        assert not np.any((a != b) & ~nan), hex(start)
         assert np.all((a[nan] & 0x7FFF) > 0x7F80)
 
 
