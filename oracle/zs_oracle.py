@@ -27,8 +27,10 @@ moments and bf16 for the working weights, so the oracle computes in fp32
 (fp64 only for the host-side scalar constants, rounded to fp32 once).
 
 Parity pins: every function below is pinned in tests/ by closed forms, brute
-force, library routines or the pages' printed numbers, except the choice of
-AdamW operation order among mathematically equal forms (see adamw_step).
+force, library routines or the pages' printed numbers. Parity unpinned: the
+choice of AdamW operation order among mathematically equal forms (see
+adamw_step); no page fixes it, and its values are pinned only by closed
+forms, exact special cases and an error bound against a float64 Adam.
 """
 from __future__ import annotations
 
