@@ -142,7 +142,7 @@ def flat_source(offsets: Sequence[int], flat_index: np.ndarray):
 
 
 # --------------------------------------------------------------- O3: reduce
-def reduce_shard(contribs: Sequence[np.ndarray], dtype: str) -> np.ndarray:
+def reduce_shard(contribs: Sequence[np.ndarray], dtype: str, scale=None) -> np.ndarray:
     """Reduce-scatter arithmetic for one shard: the mean of D contributions.
 
     [GPT8 "AllGather vs AllReduce"]: rank r receives the sum over ranks k of
@@ -153,6 +153,9 @@ def reduce_shard(contribs: Sequence[np.ndarray], dtype: str) -> np.ndarray:
     reduce dtype (bf16 [RP 2] or fp32 [GPT8 "Mixed Precision"]), are widened
     to fp32, summed left to right in rank order starting from c_0, and the
     sum is multiplied once by float32(1/D). The result stays fp32.
+
+    ``scale`` replaces 1/D as the one multiplier (rounded to float32 once):
+    1 gives the plain sum of the reduce-scatter diagram, 1/D the average.
     """
     D = len(contribs)
     if D < 1:
@@ -168,8 +171,8 @@ def reduce_shard(contribs: Sequence[np.ndarray], dtype: str) -> np.ndarray:
     s = widen(contribs[0]).copy()
     for k in range(1, D):
         s = (s + widen(contribs[k])).astype(F32)
-    inv_d = F32(1.0 / D)
-    return (s * inv_d).astype(F32)
+    mult = F32(1.0 / D) if scale is None else F32(scale)
+    return (s * mult).astype(F32)
 
 
 def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -185,7 +188,7 @@ def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def reduce_shard_hybrid(contribs: Sequence[np.ndarray], dtype: str, replicas: int,
-                        round_to_reduce_dtype: bool) -> np.ndarray:
+                        round_to_reduce_dtype: bool, scale=None) -> np.ndarray:
     """Reduce-scatter arithmetic under HYBRID_SHARD, optionally rounding
     each collective's output to the reduce dtype.
 
@@ -200,8 +203,9 @@ def reduce_shard_hybrid(contribs: Sequence[np.ndarray], dtype: str, replicas: in
     when the collectives' outputs are held in the reduce dtype, s_j is
     rounded to it. The nodes' partial sums are folded left in node order in
     fp32 and, again when rounding, rounded to the reduce dtype. The mean is
-    one multiply by float32(1/(R*D)); the result stays fp32. With R = 1 and
-    no rounding this is reduce_shard exactly.
+    one multiply by float32(1/(R*D)) (or by float32(scale) when given, as in
+    reduce_shard); the result stays fp32. With R = 1 and no rounding this is
+    reduce_shard exactly.
     """
     n = len(contribs)
     if replicas < 1 or n < 1 or n % replicas:
@@ -225,7 +229,8 @@ def reduce_shard_hybrid(contribs: Sequence[np.ndarray], dtype: str, replicas: in
         total = s if total is None else (total + s).astype(F32)
     if round_to_reduce_dtype:
         total = round_to_dtype(total, dtype)
-    return (total * F32(1.0 / n)).astype(F32)
+    mult = F32(1.0 / n) if scale is None else F32(scale)
+    return (total * mult).astype(F32)
 
 
 # --------------------------------------------------------------- O4: AdamW
@@ -302,22 +307,22 @@ def adamw_step(p: np.ndarray, m: np.ndarray, v: np.ndarray, g: np.ndarray,
     return p2, m1, v1, bf16_round(p2)
 
 
-def rank_step(p, m, v, contribs: Sequence[np.ndarray], dtype: str, hp: AdamWHP):
+def rank_step(p, m, v, contribs: Sequence[np.ndarray], dtype: str, hp: AdamWHP, scale=None):
     """The rank's shard step: reduce (O3), then AdamW (O4) on its result.
 
     This is steps 6-7 of [GPT8 "The Lifecycle of a Parameter"]: the reduce-
     scatter gives the rank its gradient shard, the optimizer updates only
     the local shard. Returns (p, m, v, w).
     """
-    g = reduce_shard(contribs, dtype)
+    g = reduce_shard(contribs, dtype, scale)
     return adamw_step(p, m, v, g, hp)
 
 
 def rank_step_hybrid(p, m, v, contribs: Sequence[np.ndarray], dtype: str, hp: AdamWHP,
-                     replicas: int, round_to_reduce_dtype: bool):
+                     replicas: int, round_to_reduce_dtype: bool, scale=None):
     """The rank's shard step with the HYBRID_SHARD / reduce-dtype reduce of
     reduce_shard_hybrid, then AdamW (O4). Returns (p, m, v, w)."""
-    g = reduce_shard_hybrid(contribs, dtype, replicas, round_to_reduce_dtype)
+    g = reduce_shard_hybrid(contribs, dtype, replicas, round_to_reduce_dtype, scale)
     return adamw_step(p, m, v, g, hp)
 
 

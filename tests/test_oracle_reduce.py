@@ -133,3 +133,54 @@ def test_inv_d_is_multiplied_not_divided():
         assert g.tobytes() == prod.tobytes()
         found += prod != quot
     assert found > 0
+
+
+# ------------------------------------------------- an explicit multiplier
+@pytest.mark.parametrize("D", [1, 3, 8, 32])
+def test_scale_one_is_the_plain_sum(D):
+    """scale = 1: the reduce-scatter diagram's sum itself, exact for small
+    integers (a closed form: Python's integer sum)."""
+    rng = np.random.default_rng(200 + D)
+    ints = rng.integers(-128, 129, size=(D, 500))
+    g = O.reduce_shard([to_bf16_bits(ints[k]) for k in range(D)], O.BF16, scale=1.0)
+    assert [float(x) for x in g] == [float(s) for s in ints.sum(axis=0)]
+
+
+@pytest.mark.parametrize("scale, den", [(0.25, 4), (0.5, 2), (2.0 ** -10, 1024)])
+def test_power_of_two_scale_is_exact(scale, den):
+    rng = np.random.default_rng(den)
+    ints = rng.integers(-1000, 1001, size=(5, 300))
+    g = O.reduce_shard([ints[k].astype(np.float32) for k in range(5)], O.FP32, scale=scale)
+    want = [Fraction(int(s), den) for s in ints.sum(axis=0)]
+    assert all(Fraction(float(a)) == b for a, b in zip(g, want))
+
+
+def test_scale_is_rounded_to_fp32_once():
+    """1/3 is not an fp32 number: the multiplier is float32(1/3), and for an
+    exact integer sum s the result is the fp32 rounding of s * float32(1/3),
+    computed here exactly with fractions."""
+    ints = np.arange(-40, 41, dtype=np.int64).reshape(1, -1).repeat(3, axis=0)
+    g = O.reduce_shard([r.astype(np.float32) for r in ints], O.FP32, scale=1.0 / 3.0)
+    third = Fraction(float(np.float32(1.0 / 3.0)))
+    for a, s in zip(g, ints.sum(axis=0)):
+        exact = Fraction(int(s)) * third       # fits a double exactly (< 31 significant bits)
+        assert float(a) == float(np.float32(float(exact)))
+
+
+def test_default_scale_is_one_over_d():
+    rng = np.random.default_rng(9)
+    x = [(rng.standard_normal(256) * 1e-3).astype(np.float32) for _ in range(7)]
+    assert O.reduce_shard(x, O.FP32).tobytes() == O.reduce_shard(x, O.FP32, scale=1.0 / 7).tobytes()
+
+
+@pytest.mark.parametrize("rnd", [False, True])
+def test_hybrid_scale_one_is_the_integer_sum(rnd):
+    """HYBRID_SHARD with scale = 1 on small integers: every partial sum is an
+    integer below 2^8, exact in bf16, so rounding changes nothing and the
+    result is Python's integer sum over all R * D contributions."""
+    rng = np.random.default_rng(31)
+    R, D = 4, 8
+    ints = rng.integers(-7, 8, size=(R * D, 400))
+    c = [to_bf16_bits(ints[k]) for k in range(R * D)]
+    g = O.reduce_shard_hybrid(c, O.BF16, R, rnd, scale=1.0)
+    assert [float(x) for x in g] == [float(s) for s in ints.sum(axis=0)]
