@@ -21,7 +21,11 @@ timed separately (one block unit, fp32) and reported under "wrap".
 Prints one JSON line. `value` is shard params/s over the whole step;
 `roofline` is the fused AdamW kernel's achieved HBM bandwidth from HIP
 events on its stream; `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload (one full block bucket, one step).
+sample of the same workload: one more step of five of the timed buckets,
+recomputed from host copies of the very inputs the GPU consumed, whose
+results `parity` compares with the GPU's bit for bit (the run exits with
+status 3 if any differ). The other workloads' shards get the same check and
+oracle timing (`cpu_baseline.per_workload`).
 """
 from __future__ import annotations
 
@@ -39,7 +43,10 @@ METRIC = "params/s and achieved HBM GB/s (% of peak) for fused reduce+AdamW shar
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 CONTRIB_POOL = 4
 PMC_FILE = os.path.join(ROOT, "profiles", "adamw_fused_llama70b_hbm_counters.md")
-KERNEL_SRC = os.path.join(ROOT, "fsdp_sharded_optimizer_zs_amd", "csrc", "zs_step.hip")
+_CSRC = os.path.join(ROOT, "fsdp_sharded_optimizer_zs_amd", "csrc")
+# what decides the fused kernel's code: its source, the headers it includes
+# (launch shape, geometry) and the compiler flags
+KERNEL_SRCS = tuple(os.path.join(_CSRC, f) for f in ("zs_step.hip", "zs_internal.h", "zs_grid.h"))
 
 
 def log(msg: str) -> None:
@@ -47,15 +54,21 @@ def log(msg: str) -> None:
 
 
 def kernel_hash() -> str:
-    """Hash of the step kernels' source with comments and whitespace removed,
-    so that the stored counters stay tied to the code, not to its comments."""
+    """Hash of what decides the step kernels' code -- their source and the
+    headers it includes, with comments and whitespace removed, and the
+    compiler flags -- so that the stored counters stay tied to the code, not
+    to its comments."""
     import re
-    with open(KERNEL_SRC) as f:
-        src = f.read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    src = re.sub(r"//[^\n]*", "", src)
-    src = re.sub(r"\s+", " ", src).strip()
-    return hashlib.sha256(src.encode()).hexdigest()[:16]
+    from fsdp_sharded_optimizer_zs_amd import build as zs_build
+    parts = []
+    for path in KERNEL_SRCS:
+        with open(path) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        parts.append(re.sub(r"\s+", " ", src).strip())
+    parts.append(" ".join(zs_build.FLAGS))
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()[:16]
 
 
 def traffic_from_profiles():
@@ -80,31 +93,79 @@ def traffic_from_profiles():
         return None
 
 
-def cpu_baseline(p, m, v, contribs, t: int, hp: dict):
-    """Time the CPU oracle on host copies of one bucket's inputs."""
+# ------------------------------------------------------------------ the oracle
+# Only the CPU-baseline leg below runs the oracle: on host copies of exactly
+# the inputs a timed GPU step consumed, it recomputes that step, times itself
+# on one host core, and compares its results with the GPU's bit for bit.
+
+def host_np(x):
+    """Host numpy copy of a device tensor (bf16 / int16 bits as uint16)."""
+    import numpy as np
+    if x.dtype.is_floating_point and x.element_size() == 2:
+        x = x.view(dtype=__import__("torch").int16)
+    a = x.cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def bf16_ulps(a, b):
+    import numpy as np
+
+    def order(h):
+        h = h.astype(np.int64)
+        return np.where(h & 0x8000, -(h & 0x7FFF), h)
+    return int(np.abs(order(a) - order(b)).max(initial=0))
+
+
+def oracle_check(snapshot, gpu_out, dtype: str, t: int, hp: dict):
+    """Run the oracle's rank step on a host snapshot (p, m, v, contributions)
+    and compare with the GPU's (p, m, v, w) for the same step. Returns
+    (params, oracle seconds, record)."""
     import numpy as np
     from oracle import zs_oracle as O
-
-    def host(x):
-        a = x.cpu().numpy()
-        return a.view(np.uint16) if a.dtype == np.int16 else a
-
-    hp_, m_, v_ = host(p), host(m), host(v)
-    cs = [host(c) for c in contribs]
-    n = hp_.size
+    p0, m0, v0, cs = snapshot
     t0 = time.perf_counter()
-    O.rank_step(hp_, m_, v_, cs, O.BF16, O.AdamWHP(step=t, **hp))
-    dt = time.perf_counter() - t0
-    return n / dt, dt, n
+    want = O.rank_step(p0, m0, v0, cs, O.BF16 if dtype == "bf16" else O.FP32,
+                       O.AdamWHP(step=t, **hp))
+    secs = time.perf_counter() - t0
+    rec = {"bit_exact": True, "max_rel_err": 0.0, "max_w_ulps": 0}
+    for name, g, w in zip(("p", "m", "v", "w"), gpu_out, want):
+        g, w = np.ascontiguousarray(g), np.ascontiguousarray(w)
+        if g.tobytes() != w.tobytes():
+            rec["bit_exact"] = False
+        if name == "w":
+            rec["max_w_ulps"] = max(rec["max_w_ulps"], bf16_ulps(g, w))
+        else:
+            d = np.abs(g.astype(np.float64) - w.astype(np.float64))
+            den = np.abs(w.astype(np.float64))
+            rel = np.where(d == 0, 0.0, d / np.maximum(den, 1e-300))
+            rec["max_rel_err"] = max(rec["max_rel_err"], float(rel.max(initial=0.0)))
+    rec["within_tolerance"] = rec["max_rel_err"] <= 1e-6 and rec["max_w_ulps"] <= 1
+    return p0.size, secs, rec
 
 
-def pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D, step_t, hp, host_buckets):
-    """Per-bucket streamed step: contributions copied into two alternating
-    staging slots on a transfer stream while the fused step of the previous
-    bucket runs on the compute stream (zs_step_pipelined). For device and
-    pinned-host sources, times the copies alone, the steps alone (sources
-    already resident) and the pipelined form, and reports how much of the
-    shorter phase the overlap hid: (copy + compute - pipelined) / min(...)."""
+def snapshot_step(zs, sl_tensors, cs, h, n=None):
+    """Host copies of (p, m, v, contributions), restricted to the first n
+    elements, then one GPU step on the whole slice; returns (snapshot, GPU
+    result restricted the same way)."""
+    p, m, v, w = sl_tensors
+    k = p.numel() if n is None else n
+    snap = (host_np(p[:k]), host_np(m[:k]), host_np(v[:k]), [host_np(c[:k]) for c in cs])
+    zs.zs_adamw_step(p, m, v, w, cs, h)
+    out = (host_np(p[:k]), host_np(m[:k]), host_np(v[:k]), host_np(w[:k]))
+    return snap, out
+
+
+def pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D, step_t, hp):
+    """Per-bucket streamed step over all of the rank's buckets:
+    contributions copied into two alternating staging slots on a transfer
+    stream while the fused step of the previous bucket runs on the compute
+    stream (zs_step_pipelined). The prefetch figure is the pinned-host form,
+    where the transfer crosses PCIe as a collective's data would cross the
+    network; the device-source form is reported as HBM contention (the copy
+    and the step share the same HBM, so there is nothing to hide). Times the
+    copies alone, the steps alone (sources already resident) and the
+    pipelined form; overlap efficiency = (copy + step - pipelined) /
+    min(copy, step), the fraction of the shorter phase hidden."""
     dev = p.device
     bmax = pool.shape[2]
     staging = (torch.empty((D, bmax), dtype=torch.int16, device=dev),
@@ -112,8 +173,9 @@ def pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D, step_t, hp, host_
     compute = torch.cuda.Stream(device=dev)
     transfer = torch.cuda.Stream(device=dev)
     res = {}
-    for kind, nb in (("device_sources", len(buckets)), ("pinned_host_sources", host_buckets)):
-        if kind == "device_sources":
+    nb = len(buckets)
+    for kind in ("pinned_host_sources", "device_sources_hbm_contention"):
+        if kind.startswith("device_sources"):
             srcs = [[pool[b % pool.shape[0], k, :sz] for k in range(D)]
                     for b, (_, sz, _, _, _) in enumerate(buckets[:nb])]
         else:
@@ -149,7 +211,7 @@ def pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D, step_t, hp, host_
         res[kind] = {"buckets": nb, "copy_ms": tc, "copy_GB_s": moved / (tc / 1e3) / 1e9,
                      "step_ms": tk, "pipelined_ms": tp,
                      "serial_ms": tc + tk,
-                     "overlap_hidden_frac": (tc + tk - tp) / min(tc, tk)}
+                     "overlap_efficiency": (tc + tk - tp) / min(tc, tk)}
         del srcs, bl
     return res
 
@@ -257,7 +319,7 @@ def hbm_directions(zs, torch, dev, read_bytes: int, write_bytes: int):
             "ideal_overlap_bound_GB_s": bound}
 
 
-def configs_leg(zs, torch, W, dev, hp, launches: int, arenas):
+def configs_leg(zs, torch, W, dev, hp, launches: int, arenas, oracle: bool):
     """The fused reduce + AdamW kernel alone on the rank shards of the other
     workloads (one launch over each whole shard, contributions resident):
     3.3M GPT at D=4, one LLaMA-7B block at D=8, the full LLaMA-7B at D=32
@@ -267,8 +329,15 @@ def configs_leg(zs, torch, W, dev, hp, launches: int, arenas):
     placed at the start of the 70B run's own four state arrays (`arenas`,
     re-initialized here), so that they sit tens of GB apart in HBM as a
     rank's separately allocated state arrays do; allocated back to back they
-    run 10-15% slower."""
+    run 10-15% slower.
+
+    With `oracle`, the first (untimed) step of each shard is also recomputed
+    by the CPU oracle from host copies of its inputs and compared bit for bit:
+    the whole shard for the 3.3M GPT, the 7B block and the ragged unit, the
+    first 2^24 params for the full 7B shard (its 32 contributions of 210M
+    params make the whole shard about a minute of oracle time)."""
     res = {}
+    oracle_n = {"gpt3m": None, "llama7b_block": None, "llama7b_full": 1 << 24, "ragged": None}
     P, M, V, WS = arenas
     busy = torch.empty(1 << 30, device=dev)        # 4 GiB: a fill of about 0.6 ms
     for name in ("gpt3m", "llama7b_block", "llama7b_full", "ragged"):
@@ -282,7 +351,19 @@ def configs_leg(zs, torch, W, dev, hp, launches: int, arenas):
         mask = W.step_mask(w, S, 1, 0, dev)
         cs = [W.contribution(w, S, 1, 0, k, dev, mask) for k in range(w.D)]
         del mask
-        zs.zs_adamw_step(p, m, v, ws, cs, dict(step=1, **hp))      # warm
+        check = None
+        if oracle:                                  # first step, checked by the oracle
+            snap, got = snapshot_step(zs, (p, m, v, ws), cs, zs.AdamWHP(step=1, **hp),
+                                      oracle_n[name])
+            n, secs, rec = oracle_check(snap, got, w.reduce_dtype, 1, hp)
+            del snap, got
+            bpp_ = 26 + w.D * es
+            check = dict(rec, params=n, oracle_s=secs, oracle_params_per_s=n / secs,
+                         oracle_GB_s=bpp_ * n / secs / 1e9, cores=1,
+                         sample="whole shard" if oracle_n[name] is None
+                         else f"first {n} params of the shard")
+        else:
+            zs.zs_adamw_step(p, m, v, ws, cs, dict(step=1, **hp))      # warm
         hps = [zs.AdamWHP(step=t, **hp) for t in range(2, 2 + launches)]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -300,7 +381,68 @@ def configs_leg(zs, torch, W, dev, hp, launches: int, arenas):
         res[name] = {"shard_params": S, "D": w.D, "reduce_dtype": w.reduce_dtype,
                      "bytes_per_param": bpp, "launch_ms": ms,
                      "params_per_s": S / (ms / 1e3), "GB_s": bpp * S / (ms / 1e3) / 1e9}
+        if check is not None:
+            res[name]["oracle"] = check
         del cs
+        torch.cuda.empty_cache()
+    del busy
+    torch.cuda.empty_cache()
+    return res
+
+
+def ragged_move_leg(zs, torch, W, dev, reps: int = 3):
+    """Pack and gather of the ragged 10,000-tensor unit (about 3.78e9
+    elements, D = 16), fp32 and bf16: the unit's tensors are separate
+    allocations, so most pieces land at another offset within 16 bytes than
+    their source. Kernel time only: the tensor table is built once and
+    reused (zs_pack_flat's `table`). Algorithmic bytes: pack es * N read +
+    es * N_pad written; gather es * N_pad read and written. Afterwards every
+    tensor is compared with its view of the gathered unit (gather(pack(x))
+    == x) and the pad must be +0."""
+    w = W.get("ragged")
+    unit = w.units[0]
+    D = w.D
+    res = {}
+    busy = torch.empty(1 << 30, device=dev)        # 4 GiB: a fill of about 0.6 ms
+    for dtype in ("f32", "bf16"):
+        ts = [t.reshape(-1) for t in W.tensor_values(unit, dtype, 5, dev)]
+        _, N, N_pad, S = zs.zs_unit_layout(unit.numels, D)
+        es = ts[0].element_size()
+        shards = [torch.empty(S, dtype=ts[0].dtype, device=dev) for _ in range(D)]
+        flat = torch.empty(N_pad, dtype=ts[0].dtype, device=dev)
+        table = zs.zs_pack_flat(ts, D, shards)               # warm, builds the table
+        zs.zs_gather_unit(shards, flat)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda.synchronize()
+        # a GPU fill ahead of each timed group keeps the GPU busy while the
+        # host queues the launches (each pack call checks the table of
+        # 10,000 tensors on the host), so that kernels are timed back to back
+        busy.fill_(1.0)
+        e[0].record()
+        for _ in range(reps):
+            zs.zs_pack_flat(ts, D, shards, table=table)
+        e[1].record()
+        torch.cuda.synchronize()
+        busy.fill_(1.0)
+        e[2].record()
+        for _ in range(reps):
+            zs.zs_gather_unit(shards, flat)
+        e[3].record()
+        torch.cuda.synchronize()
+        pack_ms, gather_ms = e[0].elapsed_time(e[1]) / reps, e[2].elapsed_time(e[3]) / reps
+        pos, exact = 0, True
+        for t in ts:
+            exact = exact and bool(torch.equal(flat[pos:pos + t.numel()], t))
+            pos += t.numel()
+        exact = exact and not bool(flat[N:].view(torch.int16 if es == 2 else torch.int32).any())
+        res[dtype] = {"tensors": len(ts), "N": N, "N_pad": N_pad, "D": D,
+                      "pack_ms": pack_ms, "pack_GB_s": es * (N + N_pad) / (pack_ms / 1e3) / 1e9,
+                      "gather_ms": gather_ms,
+                      "gather_GB_s": 2 * es * N_pad / (gather_ms / 1e3) / 1e9,
+                      "gather_of_pack_exact": exact}
+        if not exact:
+            raise SystemExit(f"ragged {dtype}: gather(pack(x)) != x")
+        del ts, shards, flat, table
         torch.cuda.empty_cache()
     del busy
     torch.cuda.empty_cache()
@@ -310,9 +452,9 @@ def configs_leg(zs, torch, W, dev, hp, launches: int, arenas):
 def reshard_ckpt_leg(zs, torch, W, dev, p, m, v, wshard, sl, D):
     """Re-shard and shard checkpoint rates: zs_reshard of one 70B block
     unit's fp32 master (855,654,400 elements) from D=8 to 6 shards (HBM
-    bytes = 2 x 4 B per element), then zs_shard_save / zs_shard_load of one
-    block bucket's rank state (p, m, v, w: 14 B per param) through a file
-    in the system temp directory."""
+    bytes = 2 x 4 B per element) and of its bf16 working shards (2 x 2 B),
+    then zs_shard_save / zs_shard_load of one block bucket's rank state (p,
+    m, v, w: 14 B per param) through a file in the system temp directory."""
     import tempfile
     unit = W.get("llama70b").units[0]
     N = unit.numel
@@ -330,6 +472,22 @@ def reshard_ckpt_leg(zs, torch, W, dev, p, m, v, wshard, sl, D):
     ms = e0.elapsed_time(e1) / 5
     res = {"reshard_block_unit_f32_8_to_6": {"elements": N, "ms": ms,
                                               "GB_s": 8 * N / (ms / 1e3) / 1e9}}
+    del src, dst
+    torch.cuda.empty_cache()
+    # the same in bf16: odd S2 puts every other new shard at an odd element
+    # offset from its sources (the shifted-load path)
+    src = [wshard[sl][:S]] + [torch.empty(S, dtype=torch.int16, device=dev) for _ in range(D - 1)]
+    dst = [torch.empty(S2, dtype=torch.int16, device=dev) for _ in range(6)]
+    zs.zs_reshard(src, N, dst)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        zs.zs_reshard(src, N, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    res["reshard_block_unit_bf16_8_to_6"] = {"elements": N, "ms": ms,
+                                             "GB_s": 4 * N / (ms / 1e3) / 1e9}
     del src, dst
     torch.cuda.empty_cache()
     Sb = sl.stop - sl.start
@@ -485,6 +643,8 @@ def main() -> int:
                     help="skip the HYBRID_SHARD (4 nodes x 8 GPUs, LLaMA-7B) step leg")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the per-bucket streamed (overlapped) step leg")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the ragged 10,000-tensor unit's pack and gather leg")
     ap.add_argument("--no-copy", action="store_true",
                     help="skip the plain 4 GiB device copy (the copy ceiling and the HBM "
                          "counter calibration)")
@@ -592,6 +752,37 @@ def main() -> int:
     ms_per_step = elapsed * 1e3 / K
     log(f"{ms_per_step:.2f} ms/step")
 
+    # CPU baseline and in-run parity: the oracle recomputes one more step of
+    # five of the timed buckets (blocks 0, 1, 39, 79 and the root) from host
+    # copies of the state and contributions those GPU steps consumed, on one
+    # host core, and the results are compared bit for bit.
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline + parity: oracle on five of the timed buckets (host copies)")
+        t_chk = args.warmup + K + 1
+        h = zs.AdamWHP(step=t_chk, **hp)
+        tot_n, tot_s, recs = 0, 0.0, []
+        for b in (0, 1, 39, 79, n_launch - 1):
+            sl, sz, cs, _, _ = buckets[b]
+            snap, got = snapshot_step(zs, (p[sl], m[sl], v[sl], wshard[sl]), cs, h)
+            n, secs, rec = oracle_check(snap, got, "bf16", t_chk, hp)
+            del snap, got
+            tot_n, tot_s = tot_n + n, tot_s + secs
+            recs.append(dict(rec, bucket=b, params=n))
+        out_parity = {"workload": "llama70b", "buckets": [r["bucket"] for r in recs],
+                      "params": tot_n, "step": t_chk,
+                      "bit_exact": all(r["bit_exact"] for r in recs),
+                      "max_rel_err": max(r["max_rel_err"] for r in recs),
+                      "max_w_ulps": max(r["max_w_ulps"] for r in recs),
+                      "tolerance": "p, m, v rel 1e-6; w 1 bf16 ulp (bit identity expected)"}
+        rate = tot_n / tot_s
+        cpu = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
+               "GB_s": (26 + 2 * D) * tot_n / tot_s / 1e9,
+               "sample": f"one step of five of the timed 70B buckets (blocks 0, 1, 39, 79 and "
+                         f"the root: {tot_n} params, D=8 bf16 contributions) from host copies "
+                         f"of the GPU's inputs, {tot_s:.1f} s of single-threaded numpy"}
+        log(f"oracle {rate / 1e6:.1f} M params/s; parity bit_exact={out_parity['bit_exact']}")
+
     # The same buckets and contributions through zs_stream_ceiling: the fused
     # kernel's streams without its arithmetic (it overwrites p, m, v, w, which
     # are re-initialized afterwards).
@@ -657,6 +848,10 @@ def main() -> int:
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
+            "traffic_source": ("committed counter summary profiles/" + os.path.basename(PMC_FILE)
+                               + ", taken on this kernel code (hash " + kernel_hash() + "); "
+                               "not measured in this run") if traffic else
+                              "no counter summary for this kernel code",
             "traffic_over_algorithmic": (traffic / bytes_per_launch) if traffic else None,
             "algorithmic_bytes_per_param": bpp,
             "algorithmic_bytes_per_launch": bytes_per_launch,
@@ -671,6 +866,8 @@ def main() -> int:
         "wrap": {"pack_block_unit_f32_ms": pack_ms,
                  "pack_GB_s": pack_bytes / (pack_ms / 1e3) / 1e9},
     }
+    if cpu is not None:
+        out["parity"] = out_parity
     if not args.no_ceiling:
         log("HBM direction probes: reads, writes and a copy alone")
         dirs = hbm_directions(zs, torch, dev, read_bytes=28, write_bytes=14)
@@ -703,7 +900,10 @@ def main() -> int:
     if not args.no_pipeline:
         log("pipeline leg: contributions streamed per bucket, overlapped with the step")
         out["pipeline"] = pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D,
-                                       args.warmup + K + 1, hp, host_buckets=16)
+                                       args.warmup + K + 1, hp)
+    if not args.no_ragged:
+        log("ragged leg: pack and gather of the 10,000-tensor unit, fp32 and bf16")
+        out["ragged_pack_gather"] = ragged_move_leg(zs, torch, W, dev)
     if not args.no_ckpt:
         log("re-shard and checkpoint leg")
         out["reshard_checkpoint"] = reshard_ckpt_leg(zs, torch, W, dev, p, m, v, wshard,
@@ -718,29 +918,27 @@ def main() -> int:
     if not args.no_configs:
         log("configs leg: the fused kernel on the other workloads' rank shards")
         out["other_workloads"] = configs_leg(zs, torch, W, dev, hp, launches=10,
-                                             arenas=(p, m, v, wshard))
-    if not args.no_cpu_baseline:
-        log("cpu baseline: oracle on five block buckets (host copies)")
-        # one step of the oracle from each bucket's current state; about 10 s
-        tot_n, tot_s = 0, 0.0
-        for sl, sz, cs, _, _ in buckets[:5]:
-            _, secs, n = cpu_baseline(p[sl], m[sl], v[sl], cs, args.warmup + K + 2, hp)
-            tot_n, tot_s = tot_n + n, tot_s + secs
-        rate = tot_n / tot_s
+                                             arenas=(p, m, v, wshard),
+                                             oracle=not args.no_cpu_baseline)
+    if cpu is not None:
         model = ""
         try:
             with open("/proc/cpuinfo") as f:
                 model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
         except OSError:
             pass
-        out["cpu_baseline"] = {
-            "value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"five block buckets of the same workload ({tot_n} params, D=8 bf16 "
-                      f"contributions), one step each, {tot_s:.1f} s of single-threaded numpy",
-            "host": {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
-                     "cpu_model": model},
-        }
+        cpu["host"] = {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+                       "cpu_model": model}
+        if "other_workloads" in out:
+            cpu["per_workload"] = {k: v["oracle"] for k, v in out["other_workloads"].items()
+                                   if "oracle" in v}
+        out["cpu_baseline"] = cpu
+        checks = [out["parity"]] + list(cpu.get("per_workload", {}).values())
+        out["parity"]["all_bit_exact"] = all(c["bit_exact"] for c in checks)
     print(json.dumps(out), flush=True)
+    if "parity" in out and not out["parity"]["all_bit_exact"]:
+        log("PARITY FAILURE: a timed GPU step differs from the oracle")
+        return 3
     return 0
 
 

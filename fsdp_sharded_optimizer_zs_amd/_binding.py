@@ -41,7 +41,8 @@ class zs_bucket(ctypes.Structure):
 
 
 class zs_reduce_opts(ctypes.Structure):
-    _fields_ = [("replicas", ctypes.c_int32), ("round_to_reduce_dtype", ctypes.c_int32)]
+    _fields_ = [("replicas", ctypes.c_int32), ("round_to_reduce_dtype", ctypes.c_int32),
+                ("scale", ctypes.c_double)]
 
 
 class zs_shard_info(ctypes.Structure):
@@ -192,19 +193,44 @@ def zs_unit_layout(numels: Sequence[int], D: int) -> Tuple[List[int], int, int, 
     return list(off), n.value, npad.value, s.value
 
 
-def zs_pack_flat(tensors: Sequence, D: int, shards: Sequence, stream=None):
-    """Pack tensors (all bf16 or all fp32, contiguous, on the device) into D
-    shard tensors of S elements each. Returns the device tensor table, which
-    the enqueued kernel reads (stream-ordered; keep it or let torch's
-    caching allocator recycle it on the same stream)."""
-    import numpy as np
-    torch = _torch()
+class PackTable:
+    """The tensor table of one unit for zs_pack_flat: a host copy (checked
+    by the library) and a device copy (read by the kernel), built once from
+    the unit's tensors so that a unit packed again (a re-wrap, a repeated
+    pack into fresh shards) does not rebuild it. It holds the tensors'
+    pointers: valid while those tensors live."""
+
+    def __init__(self, tensors: Sequence, D: int, device):
+        import numpy as np
+        torch = _torch()
+        tensors = list(tensors)
+        self.T = len(tensors)
+        self.D = int(D)
+        numels = [t.numel() for t in tensors]
+        offsets, self.N, _, self.S = zs_unit_layout(numels, D)
+        # rows are zs_tensor_ref: (ptr, numel, flat_offset), 3 x 8 bytes
+        self._host = np.empty((max(1, self.T), 3), dtype=np.int64)
+        if self.T:
+            self._host[:self.T, 0] = np.array([t.data_ptr() for t in tensors],
+                                              dtype=np.uint64).view(np.int64)
+            self._host[:self.T, 1] = numels
+            self._host[:self.T, 2] = offsets[:self.T]
+        self.device = (torch.from_numpy(self._host[:self.T]).to(device) if self.T
+                       else torch.zeros((0, 3), dtype=torch.int64, device=device))
+
+    def host_ptr(self):
+        return self._host.ctypes.data_as(ctypes.POINTER(zs_tensor_ref))
+
+    def device_ptr(self):
+        return ctypes.c_void_p(self.device.data_ptr() if self.T else None)
+
+
+def _check_pack_operands(tensors, shards, D):
     if len(shards) != D:
         raise ValueError("need exactly D shard tensors")
     ref = shards[0]
     code = _dtype_code(ref)
-    tensors = list(tensors)
-    everything = tensors + list(shards)
+    everything = list(tensors) + list(shards)
     # one pass per property, then the failing index for the message
     same = {t.dtype for t in everything}
     if not all(t.is_cuda and t.is_contiguous() for t in everything) or any(
@@ -214,26 +240,38 @@ def zs_pack_flat(tensors: Sequence, D: int, shards: Sequence, stream=None):
             _dev(t, f"tensor {i}")
             if _dtype_code(t) != code or t.element_size() != ref.element_size():
                 raise TypeError("tensors and shards must share one element type")
-    T = len(tensors)
-    numels = [t.numel() for t in tensors]
-    offsets, N, _, S = zs_unit_layout(numels, D)
-    if any(s.numel() != S for s in shards):
-        raise ValueError(f"every shard must hold S = {S} elements")
-    # the table rows are zs_tensor_ref: (ptr, numel, flat_offset), 3 x 8 bytes
-    tab = np.empty((max(1, T), 3), dtype=np.int64)
-    if T:
-        tab[:T, 0] = np.array([t.data_ptr() for t in tensors], dtype=np.uint64).view(np.int64)
-        tab[:T, 1] = numels
-        tab[:T, 2] = offsets[:T]
-    h = tab.ctypes.data_as(ctypes.POINTER(zs_tensor_ref))
-    d_table = (torch.from_numpy(tab[:T]).to(ref.device) if T
-               else torch.zeros((0, 3), dtype=torch.int64, device=ref.device))
+    return code
+
+
+def zs_pack_flat(tensors: Sequence, D: int, shards: Sequence, stream=None,
+                 table: "PackTable" = None) -> "PackTable":
+    """Pack tensors (all bf16 or all fp32, contiguous, on the device) into D
+    shard tensors of S elements each. Returns the unit's PackTable, whose
+    device copy the enqueued kernel reads (stream-ordered; keep it, or let
+    torch's caching allocator recycle it on the same stream); pass it back
+    as `table` to pack the same tensors again without rebuilding it."""
+    torch = _torch()
+    tensors = list(tensors)
+    ref = shards[0] if shards else None
+    if table is None:
+        code = _check_pack_operands(tensors, shards, D)
+        table = PackTable(tensors, D, ref.device)
+    else:
+        # the tensors were checked when the table was built (the library
+        # checks the table itself on every call); only the shards are new
+        if table.T != len(tensors) or table.D != D or len(shards) != D:
+            raise ValueError("table was built for another unit")
+        code = _check_pack_operands([], shards, D)
+        if table.T and ref.element_size() != tensors[0].element_size():
+            raise TypeError("tensors and shards must share one element type")
+    if any(s.numel() != table.S for s in shards):
+        raise ValueError(f"every shard must hold S = {table.S} elements")
     if isinstance(stream, torch.cuda.Stream):
         # the kernel reads the table on `stream`: tell the caching allocator
-        d_table.record_stream(stream)
-    _check(load().zs_pack_flat(h, ctypes.c_void_p(d_table.data_ptr() if T else None), T, code,
-                               int(D), _ptr_array(shards), S, _stream(ref, stream)))
-    return d_table
+        table.device.record_stream(stream)
+    _check(load().zs_pack_flat(table.host_ptr(), table.device_ptr(), table.T, code, int(D),
+                               _ptr_array(shards), table.S, _stream(ref, stream)))
+    return table
 
 
 def zs_reduce_shard(contribs: Sequence, grad_out, stream=None) -> None:
@@ -282,10 +320,11 @@ def _groups(contribs: Sequence, replicas: int) -> int:
 
 
 def zs_reduce_shard_ex(contribs: Sequence, grad_out, replicas: int = 1,
-                       round_to_reduce_dtype: bool = False, stream=None) -> None:
+                       round_to_reduce_dtype: bool = False, stream=None,
+                       scale: float = 0.0) -> None:
     """grad_out (fp32, S) = HYBRID_SHARD reduce of replicas groups of
     contributions (replica-major), optionally rounding each level's output to
-    the reduce dtype."""
+    the reduce dtype; scale (0 = 1 / #contributions) is the one multiplier."""
     S = grad_out.numel()
     _dev(grad_out, "grad_out")
     if grad_out.dtype != _torch().float32:
@@ -296,14 +335,15 @@ def zs_reduce_shard_ex(contribs: Sequence, grad_out, replicas: int = 1,
         if c.numel() != S or _dtype_code(c) != code:
             raise ValueError("contributions must share one dtype and hold S elements")
     D = _groups(contribs, replicas)
-    opts = zs_reduce_opts(int(replicas), 1 if round_to_reduce_dtype else 0)
+    opts = zs_reduce_opts(int(replicas), 1 if round_to_reduce_dtype else 0, float(scale))
     _check(load().zs_reduce_shard_ex(_ptr_array(contribs), D, ctypes.byref(opts), code, S,
                                      ctypes.c_void_p(grad_out.data_ptr()),
                                      _stream(grad_out, stream)))
 
 
 def zs_adamw_step_ex(p, m, v, w_out, contribs: Sequence, hp, replicas: int = 1,
-                     round_to_reduce_dtype: bool = False, stream=None) -> None:
+                     round_to_reduce_dtype: bool = False, stream=None,
+                     scale: float = 0.0) -> None:
     """zs_adamw_step with the reduce of zs_reduce_shard_ex."""
     torch = _torch()
     S = p.numel()
@@ -320,7 +360,7 @@ def zs_adamw_step_ex(p, m, v, w_out, contribs: Sequence, hp, replicas: int = 1,
         if c.numel() != S or _dtype_code(c) != code:
             raise ValueError("contributions must share one dtype and hold S elements")
     D = _groups(contribs, replicas)
-    opts = zs_reduce_opts(int(replicas), 1 if round_to_reduce_dtype else 0)
+    opts = zs_reduce_opts(int(replicas), 1 if round_to_reduce_dtype else 0, float(scale))
     h = _hp(hp)
     _check(load().zs_adamw_step_ex(ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(m.data_ptr()),
                                    ctypes.c_void_p(v.data_ptr()),
@@ -344,23 +384,10 @@ def zs_gather_unit(shards: Sequence, flat_out, stream=None) -> None:
                                  ctypes.c_void_p(flat_out.data_ptr()), _stream(flat_out, stream)))
 
 
-def zs_step_pipelined(buckets: Sequence, staging: Sequence, hp, compute=None,
-                      transfer=None) -> None:
-    """The shard step over buckets [(p, m, v, w_out, sources), ...], each
-    bucket's sources (device tensors or pinned host tensors, one dtype)
-    copied into alternating staging slots on `transfer` while the previous
-    bucket steps on `compute`. staging = (slot0, slot1): device tensors of
-    the sources' dtype, shape [n_contrib, staging_len]."""
+def _bucket_array(buckets: Sequence, n_contrib: int, code: int):
+    """zs_bucket descriptors for [(p, m, v, w_out, sources), ...], checked;
+    returns (array, pointer arrays to keep alive)."""
     torch = _torch()
-    if len(staging) != 2:
-        raise ValueError("staging must be two slot tensors")
-    s0, s1 = staging
-    for i, t in enumerate((s0, s1)):
-        _dev(t, f"staging[{i}]")
-        if t.dim() != 2 or t.shape != s0.shape or t.dtype != s0.dtype:
-            raise ValueError("staging slots must be equal [n_contrib, staging_len] tensors")
-    n_contrib, staging_len = int(s0.shape[0]), int(s0.shape[1])
-    code = _dtype_code(s0)
     arr = (zs_bucket * max(1, len(buckets)))()
     keep = []
     for b, (p, m, v, w, srcs) in enumerate(buckets):
@@ -376,13 +403,33 @@ def zs_step_pipelined(buckets: Sequence, staging: Sequence, hp, compute=None,
             raise ValueError(f"bucket {b}: need {n_contrib} sources")
         for q, c in enumerate(srcs):
             if not c.is_contiguous() or c.numel() != S or _dtype_code(c) != code:
-                raise ValueError(f"bucket {b} source {q}: contiguous, S elements, staging dtype")
+                raise ValueError(f"bucket {b} source {q}: contiguous, S elements, one dtype")
             if not c.is_cuda and c.numel() > 0 and not c.is_pinned():
                 raise ValueError(f"bucket {b} source {q}: host sources must be pinned memory")
         ptrs = _ptr_array(srcs)
         keep.append(ptrs)
         arr[b] = zs_bucket(p.data_ptr(), m.data_ptr(), v.data_ptr(), w.data_ptr(), S,
                            ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)))
+    return arr, keep
+
+
+def zs_step_pipelined(buckets: Sequence, staging: Sequence, hp, compute=None,
+                      transfer=None) -> None:
+    """The shard step over buckets [(p, m, v, w_out, sources), ...], each
+    bucket's sources (device tensors or pinned host tensors, one dtype)
+    copied into alternating staging slots on `transfer` while the previous
+    bucket steps on `compute`. staging = (slot0, slot1): device tensors of
+    the sources' dtype, shape [n_contrib, staging_len]."""
+    if len(staging) != 2:
+        raise ValueError("staging must be two slot tensors")
+    s0, s1 = staging
+    for i, t in enumerate((s0, s1)):
+        _dev(t, f"staging[{i}]")
+        if t.dim() != 2 or t.shape != s0.shape or t.dtype != s0.dtype:
+            raise ValueError("staging slots must be equal [n_contrib, staging_len] tensors")
+    n_contrib, staging_len = int(s0.shape[0]), int(s0.shape[1])
+    code = _dtype_code(s0)
+    arr, keep = _bucket_array(buckets, n_contrib, code)
     h = _hp(hp)
     _check(load().zs_step_pipelined(arr, len(buckets), n_contrib, code,
                                     ctypes.c_void_p(s0.data_ptr()), ctypes.c_void_p(s1.data_ptr()),
@@ -424,7 +471,7 @@ def zs_shard_save(path: str, rank: int, D: int, N: int, step: int, p, m, v, w,
                   stream=None) -> None:
     """Save rank `rank`'s shard (of D over N elements) after `step` steps.
     Synchronizes the stream and writes the file."""
-    S = -(-int(N) // int(D)) if D > 0 else 0
+    S = zs_unit_layout([int(N)], int(D))[3]        # the layout's S = ceil(N / D)
     info = zs_shard_info(int(rank), int(D), int(N), S, int(step))
     ptrs = _state(p, m, v, w, S)
     _check(load().zs_shard_save(os.fsencode(path), ctypes.byref(info), *ptrs,

@@ -140,13 +140,47 @@ const DeviceInfo& device_info() {
     return d;
 }
 
+namespace {
+std::mutex g_event_mu;
+std::vector<std::vector<hipEvent_t>> g_event_pool;  // per device: events not leased
+}  // namespace
+
+hipError_t EventLease::take(int n) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    dev_ = dev;
+    {
+        std::lock_guard<std::mutex> lock(g_event_mu);
+        if (g_event_pool.size() <= size_t(dev)) g_event_pool.resize(size_t(dev) + 1);
+        std::vector<hipEvent_t>& pool = g_event_pool[size_t(dev)];
+        while (int(ev_.size()) < n && !pool.empty()) {
+            ev_.push_back(pool.back());
+            pool.pop_back();
+        }
+    }
+    while (int(ev_.size()) < n) {
+        hipEvent_t x = nullptr;
+        if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
+        ev_.push_back(x);
+    }
+    return hipSuccess;
+}
+
+EventLease::~EventLease() {
+    if (ev_.empty()) return;
+    std::lock_guard<std::mutex> lock(g_event_mu);
+    std::vector<hipEvent_t>& pool = g_event_pool[size_t(dev_)];
+    pool.insert(pool.end(), ev_.begin(), ev_.end());
+}
+
 }  // namespace zs
 
 using namespace zs;
 
 ZS_EXPORT const char* zs_last_error(void) { return g_last_error.c_str(); }
 
-ZS_EXPORT int32_t zs_abi_version(void) { return 107; }
+ZS_EXPORT int32_t zs_abi_version(void) { return 200; }
 
 ZS_EXPORT zs_status zs_unit_layout(const int64_t* numels, int32_t T, int32_t D,
                                    int64_t* offsets_out, int64_t* n_out, int64_t* n_pad_out,
@@ -225,24 +259,31 @@ ZS_EXPORT zs_status zs_pack_flat(const zs_tensor_ref* h_table, const zs_tensor_r
 
 namespace {
 
-// Validates a reduce description: nd contributions per group, R groups.
+// Validates a reduce description: nd contributions per group, R groups, and
+// the fp32 multiplier of the reduced sum (1 / (R * nd) unless opts->scale is
+// set).
 zs_status check_groups(const char* who, int32_t nd, const zs_reduce_opts* opts, int* R,
-                       bool* rnd) {
+                       bool* rnd, float* mult) {
     *R = 1;
     *rnd = false;
+    double scale = 0.0;
     if (opts != nullptr) {
         if (opts->replicas < 1)
             return fail(ZS_EINVAL, "%s: replicas = %d < 1", who, opts->replicas);
         if (opts->round_to_reduce_dtype != 0 && opts->round_to_reduce_dtype != 1)
             return fail(ZS_EINVAL, "%s: round_to_reduce_dtype must be 0 or 1", who);
+        if (!std::isfinite(opts->scale))
+            return fail(ZS_EINVAL, "%s: scale must be finite", who);
         *R = opts->replicas;
         *rnd = opts->round_to_reduce_dtype == 1;
+        scale = opts->scale;
     }
     if (nd < 1 || nd > ZS_MAX_D)
         return fail(ZS_EINVAL, "%s: D = %d outside 1..%d", who, nd, ZS_MAX_D);
     if (int64_t(*R) * nd > ZS_MAX_D)
         return fail(ZS_EINVAL, "%s: replicas * D = %lld exceeds %d contributions", who,
                     (long long)(int64_t(*R) * nd), ZS_MAX_D);
+    *mult = float(scale != 0.0 ? scale : 1.0 / double(int64_t(*R) * nd));
     return ZS_OK;
 }
 
@@ -253,7 +294,8 @@ zs_status reduce_common(const char* who, const void* const* contribs, int32_t nd
     if (es == 0) return fail(ZS_EUNSUPPORTED, "%s: unknown dtype %d", who, dtype);
     int R;
     bool rnd;
-    zs_status st = check_groups(who, nd, opts, &R, &rnd);
+    float inv_n;
+    zs_status st = check_groups(who, nd, opts, &R, &rnd, &inv_n);
     if (st != ZS_OK) return st;
     if (!size_ok(S, 4)) return fail(ZS_EINVAL, "%s: S = %lld out of range", who, (long long)S);
     if (S == 0) return ok();
@@ -270,7 +312,6 @@ zs_status reduce_common(const char* who, const void* const* contribs, int32_t nd
             return fail(ZS_EALIAS, "%s: grad_out overlaps contribution %d", who, k);
         al = al && aligned(cp.p[k], 16);
     }
-    const float inv_n = float(1.0 / double(n));
     return hip_status(launch_reduce(cp, nd, R, rnd, dtype, S, inv_n, grad_out, al, stream), who);
 }
 
@@ -281,7 +322,8 @@ zs_status adamw_common(const char* who, float* p, float* m, float* v, uint16_t* 
     if (es == 0) return fail(ZS_EUNSUPPORTED, "%s: unknown dtype %d", who, dtype);
     int R;
     bool rnd;
-    zs_status st = check_groups(who, nd, opts, &R, &rnd);
+    float inv_n;
+    zs_status st = check_groups(who, nd, opts, &R, &rnd, &inv_n);
     if (st != ZS_OK) return st;
     if (!size_ok(S, 4)) return fail(ZS_EINVAL, "%s: S = %lld out of range", who, (long long)S);
     st = check_hp(hp, who);
@@ -309,7 +351,8 @@ zs_status adamw_common(const char* who, float* p, float* m, float* v, uint16_t* 
                 return fail(ZS_EALIAS, "%s: contribution %d overlaps %s", who, k, names[a]);
         al = al && aligned(cp.p[k], 16);
     }
-    const AdamConsts k = adam_consts(*hp, n);
+    AdamConsts k = adam_consts(*hp, n);
+    k.inv_n = inv_n;
     return hip_status(launch_adamw(p, m, v, w_out, S, cp, nd, R, rnd, dtype, k, al, stream), who);
 }
 

@@ -28,6 +28,7 @@ constexpr int kWave = 64;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTile = 512;
 constexpr int kPair = ZS_STEP_TILES;
+static_assert(kThreads == kBlockThreads, "grid arithmetic assumes 256-thread workgroups");
 
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -164,9 +165,7 @@ __global__ __launch_bounds__(kThreads) void probe_triad_kernel(const u32x4* __re
 hipError_t launch_streams(float* p, float* m, float* v, uint16_t* w, int64_t S,
                           const PtrPack& contribs, int n, int dtype, hipStream_t stream) {
     const int64_t npairs = S / (kPair * kTile);
-    int64_t blocks = (npairs + kWaves - 1) / kWaves;
-    if (blocks > kMaxGrid) blocks = kMaxGrid;
-    if (blocks < 1) blocks = 1;
+    const int64_t blocks = streams_grid(S, kPair);
     if (dtype == ZS_BF16)
         hipLaunchKernelGGL((streams_kernel<true>), dim3(unsigned(blocks)), dim3(kThreads), 0,
                            stream, p, m, v, w, npairs, contribs, n);
@@ -180,11 +179,8 @@ hipError_t launch_probe(int kind, void* buf, void* buf2, int64_t nvec, int per_c
                         hipStream_t stream) {
     // per_cu 0: a grid that covers the buffer (two vectors per lane for reads,
     // one otherwise); else a persistent grid of per_cu workgroups per CU
-    const int64_t lanes = kind == ZS_PROBE_READ ? (nvec + 1) / 2 : nvec;
-    const int64_t cap = per_cu > 0 ? int64_t(device_info().cu_count) * per_cu : kMaxGrid;
-    int64_t blocks = (lanes + kThreads - 1) / kThreads;
-    if (blocks > cap) blocks = cap;
-    if (blocks < 1) blocks = 1;
+    const int64_t blocks =
+        probe_grid(kind == ZS_PROBE_READ, nvec, per_cu, per_cu > 0 ? device_info().cu_count : 0);
     const dim3 grid{unsigned(blocks)}, block{unsigned(kThreads)};
     u32x4* a = static_cast<u32x4*>(buf);
     u32x4* b = static_cast<u32x4*>(buf2);

@@ -246,29 +246,31 @@ ZS_EXPORT zs_status zs_offload_step(const void* const* contribs, int32_t D, int3
                                  stream);
     if (e != hipSuccess) return hip_status(e, "zs_offload_step: reduce launch");
     // 2. g comes down chunk by chunk; 3. the host steps each chunk as soon as
-    // it has landed; 4. the chunk's bf16 shard goes back up on h2d_stream
+    // it has landed; 4. the chunk's bf16 shard goes back up on h2d_stream.
+    // Up to kAhead chunk copies are queued ahead of the host, each followed
+    // by a pooled event that the host waits on; chunk c + kAhead is queued
+    // (reusing chunk c's event) once the host has waited for chunk c.
+    constexpr int64_t kAhead = 8;
     const int64_t nchunks = (S + chunk - 1) / chunk;
-    std::vector<hipEvent_t> ev(size_t(nchunks), nullptr);
-    struct Release {
-        std::vector<hipEvent_t>& ev;
-        ~Release() {
-            for (hipEvent_t x : ev)
-                if (x) (void)hipEventDestroy(x);
-        }
-    } release{ev};
-    for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t ring = std::min(nchunks, kAhead);
+    EventLease ev;
+    if ((e = ev.take(int(ring))) != hipSuccess) return hip_status(e, "zs_offload_step: events");
+    auto queue_down = [&](int64_t c) {
         const int64_t lo = c * chunk, n = std::min(chunk, S - lo);
-        if ((e = hipEventCreateWithFlags(&ev[size_t(c)], hipEventDisableTiming)) != hipSuccess ||
-            (e = hipMemcpyAsync(grad_host + lo, grad_dev + lo, size_t(n) * 4,
-                                hipMemcpyDeviceToHost, stream)) != hipSuccess ||
-            (e = hipEventRecord(ev[size_t(c)], stream)) != hipSuccess)
-            return hip_status(e, "zs_offload_step: gradient copy");
-    }
+        hipError_t r = hipMemcpyAsync(grad_host + lo, grad_dev + lo, size_t(n) * 4,
+                                      hipMemcpyDeviceToHost, stream);
+        if (r == hipSuccess) r = hipEventRecord(ev.ev(int(c % ring)), stream);
+        return r;
+    };
+    for (int64_t c = 0; c < ring; ++c)
+        if ((e = queue_down(c)) != hipSuccess) return hip_status(e, "zs_offload_step: gradient copy");
     const AdamConsts k = adam_consts(*hp, 1);
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t lo = c * chunk, n = std::min(chunk, S - lo);
-        if ((e = hipEventSynchronize(ev[size_t(c)])) != hipSuccess)
+        if ((e = hipEventSynchronize(ev.ev(int(c % ring)))) != hipSuccess)
             return hip_status(e, "zs_offload_step: gradient wait");
+        if (c + ring < nchunks && (e = queue_down(c + ring)) != hipSuccess)
+            return hip_status(e, "zs_offload_step: gradient copy");
         parallel_step(p + lo, m + lo, v + lo, w_host + lo, grad_host + lo, n, k, threads);
         if ((e = hipMemcpyAsync(w_dev + lo, w_host + lo, size_t(n) * 2, hipMemcpyHostToDevice,
                                 h2d_stream)) != hipSuccess)

@@ -3,14 +3,18 @@
 #pragma once
 
 #include <stdint.h>
+#include <vector>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/zs.h"
+#include "zs_grid.h"
 
 // Launch shape of the tiled step kernels (workgroups of 256 threads, 4
 // wavefronts): ZS_STEP_TILES adjacent 512-element tiles per wavefront, and one
 // wavefront per tile group: the grid covers the whole shard (up to
-// kMaxGrid workgroups; the kernels loop in grid-stride order past that).
+// kMaxGrid workgroups, zs_grid.h; the kernels loop in grid-stride order past
+// that).
 // Measured on MI355X over the 81 buckets of a 70B rank shard: 6.17 TB/s,
 // against 6.05-6.11 for a persistent grid of one workgroup per CU (whose
 // wavefronts drift apart over a long launch, so more HBM rows are open at
@@ -21,9 +25,6 @@
 #endif
 
 namespace zs {
-
-// Largest grid any kernel of the library is launched with.
-constexpr int64_t kMaxGrid = int64_t(1) << 24;
 
 // Up to ZS_MAX_D device pointers passed by value as a kernel argument.
 struct PtrPack {
@@ -58,6 +59,40 @@ bool size_ok(int64_t S, int es);
 zs_status take_ptrs(const void* const* src, int n, int es, const char* what, PtrPack* out);
 zs_status check_hp(const zs_adamw_hp* hp, const char* who);
 AdamConsts adam_consts(const zs_adamw_hp& hp, int n_contrib);
+
+// HIP events that order work between streams, reused across calls so that
+// no per-step path creates a runtime object: a lease takes n events from the
+// current device's pool (creating them only when the pool runs short) and
+// gives them back when it goes out of scope. An event may be recorded again
+// once the waits that used it have been enqueued, so a returned event can
+// serve the next call at once. Pooled events live until the process ends.
+class EventLease {
+  public:
+    EventLease() = default;
+    EventLease(const EventLease&) = delete;
+    EventLease& operator=(const EventLease&) = delete;
+    ~EventLease();
+    hipError_t take(int n);  // ev(0) .. ev(n - 1) valid afterwards
+    hipEvent_t ev(int i) const { return ev_[size_t(i)]; }
+
+  private:
+    int dev_ = -1;
+    std::vector<hipEvent_t> ev_;
+};
+
+// The pipelined step (zs_pipeline.cpp), shared by its two entry points:
+// argument and aliasing checks (buckets of at most max_bucket elements;
+// staging slots of slot_elems elements each), then the enqueue, each
+// bucket in pieces of at most `piece` elements that alternate between the
+// two slots, ordered by events ev[0..4] (start, arrived[2], consumed[2]).
+zs_status pipelined_check(const char* who, const zs_bucket* buckets, int32_t n_buckets,
+                          int32_t n_contrib, int32_t dtype, const void* staging0,
+                          const void* staging1, int64_t slot_elems, int64_t max_bucket,
+                          const zs_adamw_hp* hp);
+zs_status pipelined_enqueue(const char* who, const zs_bucket* buckets, int32_t n_buckets,
+                            int32_t n_contrib, int32_t dtype, void* staging0, void* staging1,
+                            int64_t piece, const zs_adamw_hp* hp, hipStream_t compute,
+                            hipStream_t transfer, const hipEvent_t ev[5]);
 
 // Launch geometry of the device the caller's stream runs on.
 struct DeviceInfo {

@@ -4,12 +4,19 @@
 // All three are bit copies bound by HBM bandwidth. Work is split into runs
 // that are contiguous on both sides (a tensor piece that lands inside one
 // shard, or one shard landing in the flat unit). Lanes write whole 16-byte
-// destination vectors (dwordx4 stores); the source is read with dwordx4
-// loads when it is at least 4-byte aligned and with 2-byte loads when bf16
-// sits at an odd element offset (all still coalesced); loads and stores of
-// the vector body are non-temporal (each byte is touched once). The few elements
-// before the first and after the last aligned vector of a run are copied one
-// per lane. No lane ever touches a byte outside the run it copies.
+// destination vectors (dwordx4 stores). The source is read with dwordx4
+// loads: 16-byte aligned ones when source and destination share their offset
+// within 16 bytes, one load at 4-byte alignment per vector when the source is
+// dword aligned, and, for bf16 at an odd element offset, aligned loads whose
+// bytes are shifted into place in registers (v_alignbyte), each lane taking
+// the second vector it straddles from its neighbour (ds_bpermute). Loads and
+// stores of the vector body are non-temporal (each byte is touched once).
+// The few elements before the first and after the last aligned destination
+// vector of a run are copied one per lane. No lane writes a byte outside the
+// run it copies; a shifted load may read up to 15 bytes either side of the
+// run's source, always inside an aligned 16-byte vector that holds at least
+// one byte of the run (so on a page the run already touches), and never uses
+// them.
 //
 // Grids cover the work (one lane per 16-byte vector in the gather, one
 // workgroup per 8 KiB work item in pack and re-shard) rather than
@@ -34,8 +41,9 @@ constexpr int kThreads = 256;
 // every shard: 8 KiB items 5.9 (pack) and 6.0-6.2 TB/s (re-shard); 16 KiB
 // 5.7 / 5.6-6.2; 4 KiB 4.2-4.7 / 5.2 (the item's table search and index
 // arithmetic are no longer hidden); 64 KiB items launched per shard 5.4.
-constexpr int64_t kItemBytes = 8192;
-constexpr int kUnroll = 2;  // aligned vectors a lane has in flight in copy_run
+// (kItemBytes is in zs_grid.h, with the rest of the launch geometry.)
+static_assert(kThreads == kBlockThreads, "grid arithmetic assumes 256-thread workgroups");
+constexpr int kUnroll = 2;  // vectors a lane has in flight in copy_run
 
 template <int ES>
 constexpr int64_t kItem = kItemBytes / ES;  // elements per pack / re-shard work item
@@ -55,9 +63,8 @@ struct Elem<4> {
 // (16 bytes at 16- or 4-byte alignment) to 16-byte aligned destination
 // vectors, kUnroll loads in flight per lane before their stores.
 template <typename V>
-__device__ __forceinline__ void copy_vecs(u32x4* __restrict__ db, const char* sb, int64_t body,
-                                          int64_t tid, int64_t nthr) {
-    const V* s4 = reinterpret_cast<const V*>(sb);
+__device__ __forceinline__ void copy_vecs(u32x4* __restrict__ db, const V* __restrict__ s4,
+                                          int64_t body, int64_t tid, int64_t nthr) {
     int64_t i = tid;
     for (; i + (kUnroll - 1) * nthr < body; i += kUnroll * nthr) {
         u32x4 x[kUnroll];
@@ -66,11 +73,70 @@ __device__ __forceinline__ void copy_vecs(u32x4* __restrict__ db, const char* sb
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(x[u], db + i + u * nthr);
     }
-    for (; i < body; i += nthr) __builtin_nontemporal_store(__builtin_nontemporal_load(s4 + i), db + i);
+    for (; i < body; i += nthr)
+        __builtin_nontemporal_store(u32x4(__builtin_nontemporal_load(s4 + i)), db + i);
+}
+
+// bf16 at an odd element offset: destination vector i is source bytes
+// [16 i + 4 W + 2, +16) of the aligned source a4, i.e. the words of the
+// aligned vectors a4[i] and a4[i + 1] shifted down by W words and 2 bytes.
+// Lane l of a wavefront covers vector i = i0 + l and loads a4[i] only;
+// a4[i + 1] is the next lane's load, fetched across lanes (ds_bpermute),
+// except for the wavefront's last lane, which loads it itself (the run's
+// last vector i = body - 1 takes it from the lane that loads a4[body], which
+// holds the run's last bytes). Every lane runs the same trip count (i0 is
+// the same for the whole wavefront); tid % 64 is the lane and nthr a
+// multiple of 64. On MI355X this replaced eight 2-byte loads per vector
+// (re-shard of the ragged 10,000-tensor unit in bf16, 16 -> 12 shards:
+// 6.10-6.13 -> 6.26-6.33 TB/s, same process and buffers); two aligned loads
+// per lane instead of the cross-lane fetch ran 3-6% slower, and the same
+// shift for dword-aligned sources (in place of one unaligned dwordx4 load)
+// 5-8% slower.
+template <int W>
+__device__ __forceinline__ void copy_vecs_odd(u32x4* __restrict__ db,
+                                              const u32x4* __restrict__ a4, int64_t body,
+                                              int64_t tid, int64_t nthr) {
+    const int lane = int(tid & 63);
+    for (int64_t i0 = tid - lane; i0 < body; i0 += kUnroll * nthr) {
+        // every load of the iteration goes out at once, the last lane's
+        // extra vector with them (issued after the cross-lane fetch, it came
+        // when the neighbouring wavefront's non-temporal load of the same
+        // line had left L2 already: 5% more HBM reads)
+        u32x4 lo[kUnroll], hi[kUnroll], own[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = i0 + u * nthr + lane;
+            lo[u] = i <= body ? __builtin_nontemporal_load(a4 + i) : u32x4{0u, 0u, 0u, 0u};
+            own[u] = (lane == 63 && i < body) ? __builtin_nontemporal_load(a4 + i + 1)
+                                             : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                hi[u][k] = uint32_t(
+                    __builtin_amdgcn_ds_bpermute(((lane + 1) & 63) << 2, int(lo[u][k])));
+            if (lane == 63) hi[u] = own[u];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = i0 + u * nthr + lane;
+            if (i < body) {
+                const uint32_t x[8] = {lo[u][0], lo[u][1], lo[u][2], lo[u][3],
+                                       hi[u][0], hi[u][1], hi[u][2], hi[u][3]};
+                u32x4 out;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    out[k] = __builtin_amdgcn_alignbyte(x[k + W + 1], x[k + W], 2);
+                __builtin_nontemporal_store(out, db + i);
+            }
+        }
+    }
 }
 
 // Copy n elements of ES bytes from src to dst. The calling threads are
-// numbered tid in [0, nthr); each element is written by exactly one of them.
+// numbered tid in [0, nthr), nthr a multiple of 64 with tid % 64 the lane in
+// the wavefront; each element is written by exactly one of them.
 template <int ES>
 __device__ __forceinline__ void copy_run(char* dst, const char* src, int64_t n, int64_t tid,
                                          int64_t nthr) {
@@ -86,22 +152,21 @@ __device__ __forceinline__ void copy_run(char* dst, const char* src, int64_t n, 
         const int64_t e = head + body * V + (tid - head);
         reinterpret_cast<T*>(dst)[e] = reinterpret_cast<const T*>(src)[e];
     }
+    if (body <= 0) return;
     u32x4* db = reinterpret_cast<u32x4*>(dst + head * ES);
-    const char* sb = src + head * ES;
-    const uintptr_t sa = reinterpret_cast<uintptr_t>(sb);
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(src + head * ES);
     if ((sa & 15) == 0) {
-        copy_vecs<u32x4>(db, sb, body, tid, nthr);
+        copy_vecs(db, reinterpret_cast<const u32x4*>(sa), body, tid, nthr);
     } else if ((sa & 3) == 0) {
         // a dword-aligned source still loads as one dwordx4 per vector
-        copy_vecs<u32x4_a4>(db, sb, body, tid, nthr);
+        copy_vecs(db, reinterpret_cast<const u32x4_a4*>(sa), body, tid, nthr);
     } else {  // 2-byte elements at an odd element offset
-        const uint16_t* s1 = reinterpret_cast<const uint16_t*>(sb);
-        for (int64_t i = tid; i < body; i += nthr) {
-            const uint16_t* s = s1 + 8 * i;
-            u32x4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = uint32_t(s[2 * e]) | (uint32_t(s[2 * e + 1]) << 16);
-            __builtin_nontemporal_store(x, db + i);
+        const u32x4* a4 = reinterpret_cast<const u32x4*>(sa & ~uintptr_t(15));
+        switch ((sa & 15) >> 2) {  // the same for every lane of the run
+            case 0: copy_vecs_odd<0>(db, a4, body, tid, nthr); break;
+            case 1: copy_vecs_odd<1>(db, a4, body, tid, nthr); break;
+            case 2: copy_vecs_odd<2>(db, a4, body, tid, nthr); break;
+            default: copy_vecs_odd<3>(db, a4, body, tid, nthr); break;
         }
     }
 }
@@ -220,9 +285,9 @@ namespace {
 template <int ES>
 hipError_t reshard_es(const PtrPack& src, int64_t S, const PtrPack& dst, int D2, int64_t S2,
                       int64_t N, hipStream_t stream) {
-    const int64_t per_shard = (S2 + kItem<ES> - 1) / kItem<ES>;
+    const int64_t per_shard = items_per_shard(S2, ES);
     const int64_t items = per_shard * D2;
-    const int64_t blocks = items < 1 ? 1 : (items < kMaxGrid ? items : kMaxGrid);
+    const int64_t blocks = item_grid(S2, ES, D2);
     hipLaunchKernelGGL((reshard_kernel<ES>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
                        src, S, dst, S2, N, per_shard, int64_t(0), items);
     return hipGetLastError();
@@ -231,9 +296,9 @@ hipError_t reshard_es(const PtrPack& src, int64_t S, const PtrPack& dst, int D2,
 template <int ES>
 hipError_t pack_es(const zs_tensor_ref* d_table, int T, int64_t N, int D, const PtrPack& shards,
                    int64_t S, hipStream_t stream) {
-    const int64_t per_shard = (S + kItem<ES> - 1) / kItem<ES>;
+    const int64_t per_shard = items_per_shard(S, ES);
     const int64_t items = per_shard * D;
-    const int64_t blocks = items < 1 ? 1 : (items < kMaxGrid ? items : kMaxGrid);
+    const int64_t blocks = item_grid(S, ES, D);
     hipLaunchKernelGGL((pack_kernel<ES>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
                        d_table, T, N, shards, S, per_shard, int64_t(0), items);
     return hipGetLastError();
@@ -264,17 +329,12 @@ hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es, void* 
         aligned = (reinterpret_cast<uintptr_t>(shards.p[r]) & 15) == 0;
     if (aligned) {
         const int64_t nv = S * es / 16, total = nv * D;
-        int64_t blocks = (total + kThreads - 1) / kThreads;
-        if (blocks > kMaxGrid) blocks = kMaxGrid;
-        if (blocks < 1) blocks = 1;
+        const int64_t blocks = gather_flat_grid(total);
         hipLaunchKernelGGL(gather_flat_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
                            shards, nv, total, reinterpret_cast<u32x4*>(flat), in_place);
         return hipGetLastError();
     }
-    const int64_t vecs = (S * es + 15) / 16 + 1;
-    int64_t blocks = (vecs + kThreads - 1) / kThreads;
-    if (blocks > kMaxGrid) blocks = kMaxGrid;
-    if (blocks < 1) blocks = 1;
+    const int64_t blocks = gather_copy_grid(S, es);
     char* f = static_cast<char*>(flat);
     for (int r = 0; r < D; ++r) {
         if ((in_place >> r) & 1) continue;

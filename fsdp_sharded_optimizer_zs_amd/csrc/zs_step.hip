@@ -481,14 +481,6 @@ __global__ __launch_bounds__(kThreads) void reduce_scalar_kernel(float* __restri
 
 // ---------------------------------------------------------------- dispatch
 
-// Workgroups for `lanes` lanes of work (elements for the scalar kernels,
-// tile groups x 64 for the tiled ones): one lane per unit of work.
-int grid_for(int64_t lanes) {
-    int64_t blocks = (lanes + kThreads - 1) / kThreads;
-    if (blocks > kMaxGrid) blocks = kMaxGrid;
-    return blocks < 1 ? 1 : int(blocks);
-}
-
 // What one launch computes: the AdamW step (out == nullptr) or the reduce
 // alone into out.
 struct Job {
@@ -505,8 +497,9 @@ struct Job {
 template <int DT, class Sum>
 hipError_t launch_job(const Job& j, const PtrPack& c, const Sum& sum, hipStream_t stream) {
     constexpr int TP = ZS_STEP_TILES;
-    const int tiled = grid_for(j.S / (TP * kTile) * kWave);
-    const int scalar = grid_for(j.S);
+    static_assert(kThreads == kBlockThreads, "grid arithmetic assumes 256-thread workgroups");
+    const unsigned tiled = unsigned(step_tiled_grid(j.S, TP));
+    const unsigned scalar = unsigned(step_scalar_grid(j.S));
     if (j.out == nullptr) {
         if (j.aligned)
             hipLaunchKernelGGL((adamw_vec_kernel<DT, Sum, TP>), dim3(tiled), dim3(kThreads), 0,

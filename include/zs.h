@@ -200,12 +200,18 @@ zs_status zs_adamw_step(float* p, float* m, float* v, uint16_t* w_out, int64_t S
                         const zs_adamw_hp* hp, hipStream_t stream);
 
 /* How the contributions of one shard are reduced (zs_reduce_shard_ex,
- * zs_adamw_step_ex). replicas = 1 and round_to_reduce_dtype = 0 is the flat
- * reduce of zs_reduce_shard / zs_adamw_step. */
+ * zs_adamw_step_ex). replicas = 1, round_to_reduce_dtype = 0 and scale = 0
+ * is the flat reduce of zs_reduce_shard / zs_adamw_step, which always
+ * multiply by 1/D (the averaged gradient); a caller that wants another
+ * multiplier (1 for the plain sum of the reduce-scatter diagram in [GPT8]
+ * "AllGather vs AllReduce", or a loss-scale factor) sets scale here. */
 typedef struct {
     int32_t replicas;               /* R >= 1 replica groups (HYBRID_SHARD nodes) */
     int32_t round_to_reduce_dtype;  /* 0 or 1: each collective's output is held
                                        in the reduce dtype                        */
+    double scale;                   /* finite; the one multiplier of the reduced
+                                       sum, rounded to fp32 once; 0 means
+                                       1 / (R * D)                                */
 } zs_reduce_opts;
 
 /*
@@ -225,14 +231,17 @@ typedef struct {
  *   t   = round_to_reduce_dtype(t)                     if opts->round...
  *   grad_out[i] = t * float(1 / (R * D))
  * where round_to_reduce_dtype is bf16 round-to-nearest-even widened back
- * (exact identity for fp32). opts == NULL means R = 1, no rounding.
+ * (exact identity for fp32); with opts->scale != 0 the last line multiplies
+ * by float(opts->scale) instead. opts == NULL means R = 1, no rounding,
+ * scale 1 / D.
  *
  *   contribs  host array of R * D device pointers (R * D <= ZS_MAX_D), each
  *             to S elements of dtype
  *   D         contributions per node, >= 1
  *   opts      host pointer or NULL
  * Other arguments and errors as zs_reduce_shard; ZS_EINVAL also for
- * replicas < 1, round_to_reduce_dtype not 0/1 or R * D > ZS_MAX_D.
+ * replicas < 1, round_to_reduce_dtype not 0/1, R * D > ZS_MAX_D or a
+ * scale that is not finite.
  */
 zs_status zs_reduce_shard_ex(const void* const* contribs, int32_t D, const zs_reduce_opts* opts,
                              int32_t dtype, int64_t S, float* grad_out, hipStream_t stream);
@@ -240,8 +249,8 @@ zs_status zs_reduce_shard_ex(const void* const* contribs, int32_t D, const zs_re
 /*
  * zs_adamw_step_ex -- zs_adamw_step with the reduce of zs_reduce_shard_ex:
  * the gradient is the grad_out value of zs_reduce_shard_ex for these
- * contributions and opts (never stored), then the AdamW update of
- * zs_adamw_step, whose constants use n_contrib = R * D.
+ * contributions and opts (never stored, scale included), then the AdamW
+ * update of zs_adamw_step.
  * Arguments and errors as zs_adamw_step and zs_reduce_shard_ex.
  */
 zs_status zs_adamw_step_ex(float* p, float* m, float* v, uint16_t* w_out, int64_t S,
@@ -359,10 +368,11 @@ typedef struct {
 /*
  * Shard checkpoints: each rank saves its own shard (p, m, v fp32 and w
  * bf16, S elements each) to its own file -- [GPT8] "Checkpointing with
- * FSDP", sharded state dict, and "Shared Storage for Checkpoints", where
- * each GPU saves its shard in parallel. A checkpoint taken at D ranks loads
- * back at D (zs_shard_load) or at any D2 (zs_shard_load_resharded), each
- * new rank reading only the byte ranges it owns from the old files.
+ * FSDP", sharded state dict, and "Shared Storage for Checkpoints": every
+ * rank writes its own shard file concurrently. A checkpoint taken at D
+ * ranks loads back at D (zs_shard_load) or at any D2
+ * (zs_shard_load_resharded), each new rank reading only the byte ranges it
+ * owns from the old files.
  *
  * File format (little-endian). Header page, bytes [0, 4096):
  *   0 char[8] "ZSSHARD1"   8 uint32 version (1)   12 uint32 header bytes (4096)

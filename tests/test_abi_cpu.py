@@ -261,6 +261,19 @@ def test_hybrid_argument_errors(lib):
         o = B.zs_reduce_opts(R, rnd)
         return lib.zs_reduce_shard_ex(arr, D, ctypes.byref(o), zs.ZS_BF16, S, out, None)
 
+    def step_scale(scale):
+        o = B.zs_reduce_opts(1, 0, scale)
+        return lib.zs_adamw_step_ex(p, m, v, w, S, arr, 8, ctypes.byref(o), zs.ZS_BF16,
+                                    ctypes.byref(_hp()), None)
+
+    def red_scale(scale):
+        o = B.zs_reduce_opts(2, 1, scale)
+        return lib.zs_reduce_shard_ex(arr, 4, ctypes.byref(o), zs.ZS_BF16, S, A + 0x40000, None)
+
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        assert step_scale(bad) == zs.ZS_EINVAL and "scale" in zs.zs_last_error()
+        assert red_scale(bad) == zs.ZS_EINVAL and "scale" in zs.zs_last_error()
+    assert ctypes.sizeof(B.zs_reduce_opts) == 16      # int32, int32, double
     assert step(8, 0, 0) == zs.ZS_EINVAL and "replicas" in zs.zs_last_error()
     assert step(8, 1, 2) == zs.ZS_EINVAL and "round_to_reduce_dtype" in zs.zs_last_error()
     assert step(8, 9, 0) == zs.ZS_EINVAL and "exceeds" in zs.zs_last_error()

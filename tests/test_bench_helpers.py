@@ -12,9 +12,10 @@ def test_committed_counters_match_the_current_kernel_source():
 
 
 def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
-    src = tmp_path / "k.hip"
+    src, hdr = tmp_path / "k.hip", tmp_path / "k.h"
     src.write_text("int f(int x) { return x + 1; }  // one\n/* two */\n")
-    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    hdr.write_text("#define TILES 2\n")
+    monkeypatch.setattr(bench, "KERNEL_SRCS", (str(src), str(hdr)))
     h0 = bench.kernel_hash()
     src.write_text("// a new comment\nint f(int x)   {\n  return x + 1; /* c */ }\n")
     assert bench.kernel_hash() == h0
@@ -22,10 +23,24 @@ def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.kernel_hash() != h0
 
 
+def test_kernel_hash_covers_headers_and_flags(tmp_path, monkeypatch):
+    from fsdp_sharded_optimizer_zs_amd import build as zs_build
+    src, hdr = tmp_path / "k.hip", tmp_path / "k.h"
+    src.write_text("int f(int x) { return x + 1; }\n")
+    hdr.write_text("#define TILES 2\n")
+    monkeypatch.setattr(bench, "KERNEL_SRCS", (str(src), str(hdr)))
+    h0 = bench.kernel_hash()
+    hdr.write_text("#define TILES 4\n")
+    h1 = bench.kernel_hash()
+    assert h1 != h0
+    monkeypatch.setattr(zs_build, "FLAGS", zs_build.FLAGS + ["-DZS_EXTRA=1"])
+    assert bench.kernel_hash() != h1
+
+
 def test_traffic_is_null_when_the_kernel_changed(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("int g() { return 0; }\n")
-    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    monkeypatch.setattr(bench, "KERNEL_SRCS", (str(src),))
     assert bench.traffic_from_profiles() is None
 
 

@@ -57,6 +57,59 @@ def test_reduce_ex_matches_oracle(dtype, R, D, rnd, offset):
     check_f32(to_np(out), want, f"reduce R={R} D={D} rnd={rnd}", exact=True)
 
 
+SCALES = [1.0, 0.5, 1.0 / 3.0, 2.0 ** -20, 1024.0]
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.FP32])
+@pytest.mark.parametrize("R,D,rnd", [(1, 8, False), (1, 5, False), (2, 4, True), (4, 8, True)])
+@pytest.mark.parametrize("scale", SCALES)
+def test_reduce_ex_scale_matches_oracle(dtype, R, D, rnd, scale):
+    """An explicit multiplier in place of 1/(R*D): 1 is the reduce-scatter's
+    plain sum, the others scale it (rounded to fp32 once)."""
+    dev = device()
+    S = 2 * 2048 * 8 + 29
+    cs = contribs(R * D, S, dtype, 300 + 10 * R + D, dev)
+    out = torch.empty(S, device=dev)
+    zs.zs_reduce_shard_ex(cs, out, replicas=R, round_to_reduce_dtype=rnd, scale=scale)
+    want = O.reduce_shard_hybrid([to_np(c) for c in cs], dtype, R, rnd, scale=scale)
+    check_f32(to_np(out), want, f"reduce R={R} D={D} rnd={rnd} scale={scale}", exact=True)
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.FP32])
+@pytest.mark.parametrize("R,D,rnd", [(1, 8, False), (2, 4, True), (3, 3, False)])
+@pytest.mark.parametrize("scale", SCALES)
+@pytest.mark.parametrize("offset", [0, 1])
+def test_adamw_ex_scale_matches_oracle(dtype, R, D, rnd, scale, offset):
+    dev = device()
+    S = 2048 * 8 + 77
+    p, m, v, w = state(S, 50 + R + D, dev, offset)
+    op, om, ov = to_np(p), np.zeros(S, np.float32), np.zeros(S, np.float32)
+    for t in (1, 2):
+        cs = contribs(R * D, S, dtype, 700 * t + 10 * R + D, dev, offset)
+        hp = dict(step=t, **HP)
+        zs.zs_adamw_step_ex(p, m, v, w, cs, hp, replicas=R, round_to_reduce_dtype=rnd,
+                            scale=scale)
+        op, om, ov, ow = O.rank_step_hybrid(op, om, ov, [to_np(c) for c in cs], dtype,
+                                            O.AdamWHP(**hp), R, rnd, scale=scale)
+    torch.cuda.synchronize()
+    what = f"R={R} D={D} rnd={rnd} scale={scale} off={offset}"
+    check_f32(to_np(p), op, what + " p", exact=True)
+    check_f32(to_np(m), om, what + " m", exact=True)
+    check_f32(to_np(v), ov, what + " v", exact=True)
+    check_bf16(to_np(w), ow, what + " w", exact=True)
+
+
+def test_scale_zero_means_the_mean():
+    """scale = 0 (the default) and scale = 1/(R*D) give the same bits."""
+    dev = device()
+    S = 4096 + 3
+    cs = contribs(6, S, O.BF16, 901, dev)
+    a, b = torch.empty(S, device=dev), torch.empty(S, device=dev)
+    zs.zs_reduce_shard_ex(cs, a, replicas=2)
+    zs.zs_reduce_shard_ex(cs, b, replicas=2, scale=1.0 / 6.0)
+    assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("dtype", [O.BF16, O.FP32])
 @pytest.mark.parametrize("R,D,rnd", CASES)
 @pytest.mark.parametrize("offset", [0, 1])
