@@ -109,6 +109,8 @@ def load() -> ctypes.CDLL:
                                                   vp, i64, P(zs_shard_info), vp]),
                 "zs_step_pipelined": (i32, [P(zs_bucket), i32, i32, i32, vp, vp, i64,
                                             P(zs_adamw_hp), vp, vp]),
+                "zs_step_pipelined_static": (i32, [P(zs_bucket), i32, i32, i32,
+                                                   P(zs_adamw_hp), vp, vp]),
                 "zs_last_error": (ctypes.c_char_p, []),
                 "zs_abi_version": (i32, []),
             }
@@ -435,6 +437,22 @@ def zs_step_pipelined(buckets: Sequence, staging: Sequence, hp, compute=None,
                                     ctypes.c_void_p(s0.data_ptr()), ctypes.c_void_p(s1.data_ptr()),
                                     staging_len, ctypes.byref(h), _stream(s0, compute),
                                     _stream(s0, transfer)))
+
+
+def zs_step_pipelined_static(buckets: Sequence, hp, compute=None, transfer=None) -> None:
+    """zs_step_pipelined with the library's own staging array (no staging
+    argument, no device allocation): buckets [(p, m, v, w_out, sources), ...]
+    with sources of one dtype, as many per bucket."""
+    if not buckets:
+        raise ValueError("need at least one bucket")
+    srcs0 = buckets[0][4]
+    n_contrib = len(srcs0)
+    code = _dtype_code(srcs0[0]) if srcs0 else ZS_F32
+    arr, keep = _bucket_array(buckets, n_contrib, code)
+    h = _hp(hp)
+    ref = buckets[0][0]
+    _check(load().zs_step_pipelined_static(arr, len(buckets), n_contrib, code, ctypes.byref(h),
+                                           _stream(ref, compute), _stream(ref, transfer)))
 
 
 def zs_reshard(src: Sequence, N: int, dst: Sequence, stream=None) -> None:

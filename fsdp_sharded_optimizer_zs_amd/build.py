@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libzs.so")
 SOURCES = ("zs_api.cpp", "zs_pipeline.cpp", "zs_ckpt.cpp", "zs_host.cpp", "zs_step.hip",
-           "zs_move.hip", "zs_diag.hip")
+           "zs_move.hip", "zs_diag.hip", "zs_static.hip")
 
 # -ffp-contract=off: no fused multiply-add in the step's arithmetic;
 # correctly rounded fp32 divide and sqrt (the HIP default, stated);

@@ -13,6 +13,8 @@
  *   zs_gather_unit   all-gather's local rebuild of a unit from its shards
  *   zs_step_pipelined  the step over a sequence of buckets, each bucket's
  *                    contribution transfer overlapped with the previous step
+ *   zs_step_pipelined_static  the same with library-owned staging, for
+ *                    callers that cannot allocate device memory
  *   zs_reshard       re-shard a unit from D to D2 shards on the device
  *   zs_shard_save, zs_shard_load, zs_shard_load_resharded, zs_shard_info_read
  *                    per-rank shard checkpoints, resumable at any D2
@@ -332,6 +334,36 @@ typedef struct {
 zs_status zs_step_pipelined(const zs_bucket* buckets, int32_t n_buckets, int32_t n_contrib,
                             int32_t dtype, void* staging0, void* staging1, int64_t staging_len,
                             const zs_adamw_hp* hp, hipStream_t compute, hipStream_t transfer);
+
+/*
+ * zs_step_pipelined_static -- zs_step_pipelined for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The caller passes the buckets (inputs and
+ * outputs) only; the staging slots live in a device array of the library
+ * (two slots of 64 MiB, 128 MiB in all on each device that runs this call,
+ * held until the process ends). A bucket whose n_contrib contributions do
+ * not fit one slot is staged and stepped in pieces of at most
+ * P = floor(64 MiB / (n_contrib * element size) / 1024) * 1024 elements
+ * (P >= 262,144), so there is no limit on a bucket's size; the results are
+ * bit-identical to zs_step_pipelined (and to zs_adamw_step on every bucket),
+ * the step being elementwise. Sources may be device or pinned host memory.
+ *
+ * The first call on a device sets up that device's staging array address and
+ * five events; no call allocates device memory or calls an allocating
+ * library routine. Every call on one device shares the same staging array:
+ * calls whose work overlaps in time on one device (enqueued on different
+ * compute streams, or from several threads) race on it and on its events;
+ * calls enqueued one after another on the same compute stream are ordered
+ * (each call's first copies wait for all work already on `compute`).
+ *
+ *   buckets, n_buckets, n_contrib, dtype, hp, compute, transfer
+ *                as zs_step_pipelined (no staging arguments)
+ * Errors: as zs_step_pipelined; ZS_EHIP also when the staging array's
+ * set-up fails.
+ */
+zs_status zs_step_pipelined_static(const zs_bucket* buckets, int32_t n_buckets,
+                                   int32_t n_contrib, int32_t dtype, const zs_adamw_hp* hp,
+                                   hipStream_t compute, hipStream_t transfer);
 
 /*
  * zs_reshard -- re-shard one unit from D shards to D2 shards, on the device.

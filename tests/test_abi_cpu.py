@@ -36,6 +36,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("zs_unit_layout", "zs_pack_flat", "zs_reduce_shard", "zs_adamw_step",
               "zs_gather_unit", "zs_step_pipelined", "zs_reduce_shard_ex", "zs_adamw_step_ex",
+              "zs_step_pipelined_static",
               "zs_reshard", "zs_shard_save", "zs_shard_info_read", "zs_shard_load",
               "zs_shard_load_resharded", "zs_adamw_step_host", "zs_offload_step",
               "zs_stream_ceiling", "zs_hbm_probe", "zs_last_error", "zs_abi_version"):
