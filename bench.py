@@ -390,7 +390,7 @@ def configs_leg(zs, torch, W, dev, hp, launches: int, arenas, oracle: bool):
     return res
 
 
-def ragged_move_leg(zs, torch, W, dev, reps: int = 3):
+def ragged_move_leg(zs, torch, W, dev, reps: int = 5):
     """Pack and gather of the ragged 10,000-tensor unit (about 3.78e9
     elements, D = 16), fp32 and bf16: the unit's tensors are separate
     allocations, so most pieces land at another offset within 16 bytes than
@@ -414,16 +414,18 @@ def ragged_move_leg(zs, torch, W, dev, reps: int = 3):
         zs.zs_gather_unit(shards, flat)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         torch.cuda.synchronize()
-        # a GPU fill ahead of each timed group keeps the GPU busy while the
-        # host queues the launches (each pack call checks the table of
-        # 10,000 tensors on the host), so that kernels are timed back to back
-        busy.fill_(1.0)
+        # GPU fills ahead of each timed group (about 2.4 ms) keep the GPU busy
+        # while the host queues the launches (each pack call checks the table
+        # of 10,000 tensors on the host), so that kernels are timed back to back
+        for _ in range(4):
+            busy.fill_(1.0)
         e[0].record()
         for _ in range(reps):
             zs.zs_pack_flat(ts, D, shards, table=table)
         e[1].record()
         torch.cuda.synchronize()
-        busy.fill_(1.0)
+        for _ in range(4):
+            busy.fill_(1.0)
         e[2].record()
         for _ in range(reps):
             zs.zs_gather_unit(shards, flat)

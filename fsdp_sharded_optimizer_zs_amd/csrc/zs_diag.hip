@@ -83,13 +83,29 @@ __device__ __forceinline__ void tiles(f32x4* __restrict__ p4, f32x4* __restrict_
             sb[u] = slot[kWave + lane];
             wave_sync();
         }
+    }
+    // stores stream by stream over the tile group, as in the fused kernel
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
         const int64_t a = (tile0 + u) * (kTile / 4) + lane, b = a + kWave;
         __builtin_nontemporal_store(pa[u] + ma[u], p4 + a);
         __builtin_nontemporal_store(pb[u] + mb[u], p4 + b);
+    }
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+        const int64_t a = (tile0 + u) * (kTile / 4) + lane, b = a + kWave;
         __builtin_nontemporal_store(va[u], m4 + a);
         __builtin_nontemporal_store(vb[u], m4 + b);
+    }
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+        const int64_t a = (tile0 + u) * (kTile / 4) + lane, b = a + kWave;
         __builtin_nontemporal_store(pa[u], v4 + a);
         __builtin_nontemporal_store(pb[u], v4 + b);
+    }
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+        const int64_t a = (tile0 + u) * (kTile / 4) + lane, b = a + kWave;
         __builtin_nontemporal_store(u32x2{sa[u].x, sa[u].y}, w2 + a);
         __builtin_nontemporal_store(u32x2{sb[u].x, sb[u].y}, w2 + b);
     }

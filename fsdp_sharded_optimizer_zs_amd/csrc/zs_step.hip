@@ -328,7 +328,7 @@ __device__ __forceinline__ void run_to_split(float (&g)[kVec], f32x4* slot, int 
 }
 
 // AdamW on TP adjacent tiles from tile0, lane `lane`: all state loads, then
-// the contributions of every tile, then the arithmetic and the stores.
+// the contributions of every tile, then the arithmetic, then the stores.
 template <int DT, int TP, class Sum>
 __device__ __forceinline__ void adamw_tiles(f32x4* __restrict__ p4, f32x4* __restrict__ m4,
                                             f32x4* __restrict__ v4, u32x2* __restrict__ w2,
@@ -353,33 +353,51 @@ __device__ __forceinline__ void adamw_tiles(f32x4* __restrict__ p4, f32x4* __res
 #pragma unroll
         for (int u = 0; u < TP; ++u) run_to_split(g[u], slot, lane);
     }
+    // every tile's arithmetic, then the stores stream by stream (p of all
+    // tiles, then m, v and w), so that each stream's run of the tile group
+    // leaves in consecutive instructions (70B buckets: 0.2-0.3% faster than
+    // storing tile by tile, same process and buffers)
+    float pp[TP][kVec], mm[TP][kVec], vv[TP][kVec];
+    u32x2 wa[TP], wb[TP];
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pp[u][e] = pa[u][e], pp[u][4 + e] = pb[u][e];
+            mm[u][e] = ma[u][e], mm[u][4 + e] = mb[u][e];
+            vv[u][e] = va[u][e], vv[u][4 + e] = vb[u][e];
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) adamw1(pp[u][e], mm[u][e], vv[u][e], g[u][e], k);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            wa[u][e] = f32_to_bf16(pp[u][2 * e]) | (f32_to_bf16(pp[u][2 * e + 1]) << 16);
+            wb[u][e] = f32_to_bf16(pp[u][4 + 2 * e]) | (f32_to_bf16(pp[u][5 + 2 * e]) << 16);
+        }
+    }
 #pragma unroll
     for (int u = 0; u < TP; ++u) {
         const int64_t a = (tile0 + u) * (kTile / 4) + lane;
-        const int64_t b = a + kWave;
-        float pp[kVec], mm[kVec], vv[kVec];
+        st_once(f32x4{pp[u][0], pp[u][1], pp[u][2], pp[u][3]}, p4 + a);
+        st_once(f32x4{pp[u][4], pp[u][5], pp[u][6], pp[u][7]}, p4 + a + kWave);
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            pp[e] = pa[u][e], pp[4 + e] = pb[u][e];
-            mm[e] = ma[u][e], mm[4 + e] = mb[u][e];
-            vv[e] = va[u][e], vv[4 + e] = vb[u][e];
-        }
+    for (int u = 0; u < TP; ++u) {
+        const int64_t a = (tile0 + u) * (kTile / 4) + lane;
+        st_once(f32x4{mm[u][0], mm[u][1], mm[u][2], mm[u][3]}, m4 + a);
+        st_once(f32x4{mm[u][4], mm[u][5], mm[u][6], mm[u][7]}, m4 + a + kWave);
+    }
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) adamw1(pp[e], mm[e], vv[e], g[u][e], k);
-        u32x2 wa, wb;
+    for (int u = 0; u < TP; ++u) {
+        const int64_t a = (tile0 + u) * (kTile / 4) + lane;
+        st_once(f32x4{vv[u][0], vv[u][1], vv[u][2], vv[u][3]}, v4 + a);
+        st_once(f32x4{vv[u][4], vv[u][5], vv[u][6], vv[u][7]}, v4 + a + kWave);
+    }
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            wa[e] = f32_to_bf16(pp[2 * e]) | (f32_to_bf16(pp[2 * e + 1]) << 16);
-            wb[e] = f32_to_bf16(pp[4 + 2 * e]) | (f32_to_bf16(pp[5 + 2 * e]) << 16);
-        }
-        st_once(f32x4{pp[0], pp[1], pp[2], pp[3]}, p4 + a);
-        st_once(f32x4{pp[4], pp[5], pp[6], pp[7]}, p4 + b);
-        st_once(f32x4{mm[0], mm[1], mm[2], mm[3]}, m4 + a);
-        st_once(f32x4{mm[4], mm[5], mm[6], mm[7]}, m4 + b);
-        st_once(f32x4{vv[0], vv[1], vv[2], vv[3]}, v4 + a);
-        st_once(f32x4{vv[4], vv[5], vv[6], vv[7]}, v4 + b);
-        st_once(wa, w2 + a);
-        st_once(wb, w2 + b);
+    for (int u = 0; u < TP; ++u) {
+        const int64_t a = (tile0 + u) * (kTile / 4) + lane;
+        st_once(wa[u], w2 + a);
+        st_once(wb[u], w2 + a + kWave);
     }
 }
 
