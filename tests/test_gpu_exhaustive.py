@@ -51,3 +51,52 @@ def test_working_shard_rounding_all_fp32_patterns():
         print(f"patterns {a:#011x}..{a + CHUNK - 1:#011x} ok", flush=True)
     del p, m, v, w, g
     torch.cuda.empty_cache()
+
+
+def test_element_at_a_time_path_past_the_grid_cap():
+    """Buffers one element off 16-byte alignment take the element-at-a-time
+    kernels, one lane per element; at S = 2^32 + 4099 their grid is capped
+    at 2^24 - 1 workgroups of 256 (the launch's thread count must fit in 32
+    bits) and the kernels loop in grid-stride order over the rest. The fused
+    step and the reduce are checked against the oracle on sampled positions,
+    both ends, and every element around the first stride boundary
+    (2^32 - 256) and past 2^32."""
+    from gpu_util import SampledRank, sample_indices, to_np, check_f32
+    dev = device()
+    S = (1 << 32) + 4099
+    stride = ((1 << 32) - 1) // 256 * 256          # threads of the capped grid: 2^32 - 256
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(321)
+
+    def fill_normal(t, std):
+        for a in range(0, S, CHUNK):
+            b = min(S, a + CHUNK)
+            torch.randn(b - a, generator=gen, device=dev, out=t[a:b]).mul_(std)
+
+    p = torch.empty(S + 1, device=dev)[1:]          # 4 bytes off: not 16-byte aligned
+    fill_normal(p, 0.02)
+    m = torch.zeros(S + 1, device=dev)[1:]
+    v = torch.zeros(S + 1, device=dev)[1:]
+    w = torch.empty(S + 1, dtype=torch.int16, device=dev)[1:]
+    c = torch.empty(S, dtype=torch.int16, device=dev)
+    tmp = torch.empty(CHUNK, device=dev)
+    for a in range(0, S, CHUNK):
+        b = min(S, a + CHUNK)
+        torch.randn(b - a, generator=gen, device=dev, out=tmp[:b - a]).mul_(1e-3)
+        c[a:b].copy_(tmp[:b - a].to(torch.bfloat16).view(torch.int16))
+    del tmp
+    extra = torch.cat([torch.arange(stride - 300, stride + 300, device=dev),
+                       torch.arange((1 << 32) - 300, (1 << 32) + 300, device=dev)])
+    idx = torch.unique(torch.cat([sample_indices(S, 100_000, 77, dev), extra]))
+    orc = SampledRank(idx, p, m, v)
+    hp = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+    zs.zs_adamw_step(p, m, v, w, [c], hp)
+    orc.step([c], O.BF16, O.AdamWHP(**hp))
+    orc.check(p, m, v, w, "S = 2^32 + 4099, misaligned")
+    del m, v, w
+    out = torch.empty(S + 1, device=dev)[1:]
+    zs.zs_reduce_shard([c, c], out)
+    want = O.reduce_shard([to_np(c[idx]), to_np(c[idx])], O.BF16)
+    check_f32(to_np(out[idx]), want, "reduce S = 2^32 + 4099, misaligned", exact=True)
+    del p, c, out
+    torch.cuda.empty_cache()
