@@ -13,7 +13,7 @@ from ._binding import (  # noqa: F401
     zs_unit_layout, zs_reshard, zs_shard_save, zs_shard_info_read, zs_shard_load,
     zs_shard_load_resharded, ZS_EIO, zs_adamw_step_host, zs_offload_step, zs_stream_ceiling,
     zs_hbm_probe, ZS_PROBE_READ, ZS_PROBE_WRITE, ZS_PROBE_COPY, ZS_PROBE_TRIAD, PackTable,
-    zs_step_pipelined_static,
+    zs_step_pipelined_static, ZS_W_STREAM, ZS_W_KEEP,
 )
 
 __all__ = [

@@ -40,9 +40,13 @@ class zs_bucket(ctypes.Structure):
                 ("sources", ctypes.POINTER(ctypes.c_void_p))]
 
 
+ZS_W_STREAM, ZS_W_KEEP = 0, 1
+
+
 class zs_reduce_opts(ctypes.Structure):
     _fields_ = [("replicas", ctypes.c_int32), ("round_to_reduce_dtype", ctypes.c_int32),
-                ("scale", ctypes.c_double)]
+                ("scale", ctypes.c_double), ("working_shard_hint", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class zs_shard_info(ctypes.Structure):
@@ -345,8 +349,10 @@ def zs_reduce_shard_ex(contribs: Sequence, grad_out, replicas: int = 1,
 
 def zs_adamw_step_ex(p, m, v, w_out, contribs: Sequence, hp, replicas: int = 1,
                      round_to_reduce_dtype: bool = False, stream=None,
-                     scale: float = 0.0) -> None:
-    """zs_adamw_step with the reduce of zs_reduce_shard_ex."""
+                     scale: float = 0.0, keep_working_shard: bool = False) -> None:
+    """zs_adamw_step with the reduce of zs_reduce_shard_ex; keep_working_shard
+    stores the bf16 working shard with cache-allocating stores, for a caller
+    that reads it right after (the unit's all-gather)."""
     torch = _torch()
     S = p.numel()
     for name, t in (("p", p), ("m", m), ("v", v)):
@@ -362,7 +368,8 @@ def zs_adamw_step_ex(p, m, v, w_out, contribs: Sequence, hp, replicas: int = 1,
         if c.numel() != S or _dtype_code(c) != code:
             raise ValueError("contributions must share one dtype and hold S elements")
     D = _groups(contribs, replicas)
-    opts = zs_reduce_opts(int(replicas), 1 if round_to_reduce_dtype else 0, float(scale))
+    opts = zs_reduce_opts(int(replicas), 1 if round_to_reduce_dtype else 0, float(scale),
+                          ZS_W_KEEP if keep_working_shard else ZS_W_STREAM, 0)
     h = _hp(hp)
     _check(load().zs_adamw_step_ex(ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(m.data_ptr()),
                                    ctypes.c_void_p(v.data_ptr()),

@@ -119,6 +119,7 @@ AdamConsts adam_consts(const zs_adamw_hp& hp, int n_contrib) {
     k.bc2s = float(std::sqrt(1.0 - b2t));
     k.eps = float(hp.eps);
     k.inv_n = float(1.0 / double(n_contrib));
+    k.keep_w = 0;
     return k;
 }
 
@@ -263,11 +264,17 @@ namespace {
 // the fp32 multiplier of the reduced sum (1 / (R * nd) unless opts->scale is
 // set).
 zs_status check_groups(const char* who, int32_t nd, const zs_reduce_opts* opts, int* R,
-                       bool* rnd, float* mult) {
+                       bool* rnd, float* mult, int* keep_w) {
     *R = 1;
     *rnd = false;
+    *keep_w = 0;
     double scale = 0.0;
     if (opts != nullptr) {
+        if (opts->working_shard_hint != ZS_W_STREAM && opts->working_shard_hint != ZS_W_KEEP)
+            return fail(ZS_EINVAL, "%s: working_shard_hint = %d is neither ZS_W_STREAM nor ZS_W_KEEP",
+                        who, opts->working_shard_hint);
+        if (opts->reserved != 0) return fail(ZS_EINVAL, "%s: reserved must be 0", who);
+        *keep_w = opts->working_shard_hint == ZS_W_KEEP ? 1 : 0;
         if (opts->replicas < 1)
             return fail(ZS_EINVAL, "%s: replicas = %d < 1", who, opts->replicas);
         if (opts->round_to_reduce_dtype != 0 && opts->round_to_reduce_dtype != 1)
@@ -295,7 +302,8 @@ zs_status reduce_common(const char* who, const void* const* contribs, int32_t nd
     int R;
     bool rnd;
     float inv_n;
-    zs_status st = check_groups(who, nd, opts, &R, &rnd, &inv_n);
+    int keep_w;  // no working shard here: the hint is ignored
+    zs_status st = check_groups(who, nd, opts, &R, &rnd, &inv_n, &keep_w);
     if (st != ZS_OK) return st;
     if (!size_ok(S, 4)) return fail(ZS_EINVAL, "%s: S = %lld out of range", who, (long long)S);
     if (S == 0) return ok();
@@ -323,7 +331,8 @@ zs_status adamw_common(const char* who, float* p, float* m, float* v, uint16_t* 
     int R;
     bool rnd;
     float inv_n;
-    zs_status st = check_groups(who, nd, opts, &R, &rnd, &inv_n);
+    int keep_w;
+    zs_status st = check_groups(who, nd, opts, &R, &rnd, &inv_n, &keep_w);
     if (st != ZS_OK) return st;
     if (!size_ok(S, 4)) return fail(ZS_EINVAL, "%s: S = %lld out of range", who, (long long)S);
     st = check_hp(hp, who);
@@ -353,6 +362,7 @@ zs_status adamw_common(const char* who, float* p, float* m, float* v, uint16_t* 
     }
     AdamConsts k = adam_consts(*hp, n);
     k.inv_n = inv_n;
+    k.keep_w = keep_w;
     return hip_status(launch_adamw(p, m, v, w_out, S, cp, nd, R, rnd, dtype, k, al, stream), who);
 }
 

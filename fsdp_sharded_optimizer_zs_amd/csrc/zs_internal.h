@@ -42,6 +42,7 @@ struct AdamConsts {
     float bc2s;   // sqrt(1 - beta2^t)
     float eps;    // eps
     float inv_n;  // 1 / n_contrib
+    int keep_w;   // 1: the working shard is stored with cache-allocating stores
 };
 
 // Host-side helpers shared by the entry points (zs_api.cpp).

@@ -202,11 +202,25 @@ zs_status zs_adamw_step(float* p, float* m, float* v, uint16_t* w_out, int64_t S
                         const zs_adamw_hp* hp, hipStream_t stream);
 
 /* How the contributions of one shard are reduced (zs_reduce_shard_ex,
- * zs_adamw_step_ex). replicas = 1, round_to_reduce_dtype = 0 and scale = 0
- * is the flat reduce of zs_reduce_shard / zs_adamw_step, which always
- * multiply by 1/D (the averaged gradient); a caller that wants another
- * multiplier (1 for the plain sum of the reduce-scatter diagram in [GPT8]
- * "AllGather vs AllReduce", or a loss-scale factor) sets scale here. */
+ * zs_adamw_step_ex), and how the step's bf16 working shard is stored.
+ * All fields 0 except replicas = 1 is the flat reduce of zs_reduce_shard /
+ * zs_adamw_step, which always multiply by 1/D (the averaged gradient); a
+ * caller that wants another multiplier (1 for the plain sum of the
+ * reduce-scatter diagram in [GPT8] "AllGather vs AllReduce", or a
+ * loss-scale factor) sets scale here.
+ *
+ * working_shard_hint (zs_adamw_step_ex only; zs_reduce_shard_ex ignores it):
+ *   ZS_W_STREAM  non-temporal stores, as every other stream of the step: the
+ *                default, for a working shard read much later;
+ *   ZS_W_KEEP    ordinary stores that allocate in the caches (L2 and the
+ *                memory-side Infinity Cache), for a caller that reads the
+ *                working shard right after -- the all-gather of the same unit,
+ *                [ZT] section 5.1 / [GPT8] "The Lifecycle of a Parameter".
+ *                The gather then reads it from the cache, so the shard crosses
+ *                HBM once (written back later) instead of twice (written, then
+ *                read). The values are the same bits either way. */
+#define ZS_W_STREAM 0
+#define ZS_W_KEEP   1
 typedef struct {
     int32_t replicas;               /* R >= 1 replica groups (HYBRID_SHARD nodes) */
     int32_t round_to_reduce_dtype;  /* 0 or 1: each collective's output is held
@@ -214,6 +228,8 @@ typedef struct {
     double scale;                   /* finite; the one multiplier of the reduced
                                        sum, rounded to fp32 once; 0 means
                                        1 / (R * D)                                */
+    int32_t working_shard_hint;     /* ZS_W_STREAM or ZS_W_KEEP                   */
+    int32_t reserved;               /* must be 0                                  */
 } zs_reduce_opts;
 
 /*
@@ -242,8 +258,8 @@ typedef struct {
  *   D         contributions per node, >= 1
  *   opts      host pointer or NULL
  * Other arguments and errors as zs_reduce_shard; ZS_EINVAL also for
- * replicas < 1, round_to_reduce_dtype not 0/1, R * D > ZS_MAX_D or a
- * scale that is not finite.
+ * replicas < 1, round_to_reduce_dtype not 0/1, R * D > ZS_MAX_D, a scale
+ * that is not finite, an unknown working_shard_hint or reserved != 0.
  */
 zs_status zs_reduce_shard_ex(const void* const* contribs, int32_t D, const zs_reduce_opts* opts,
                              int32_t dtype, int64_t S, float* grad_out, hipStream_t stream);
@@ -252,7 +268,8 @@ zs_status zs_reduce_shard_ex(const void* const* contribs, int32_t D, const zs_re
  * zs_adamw_step_ex -- zs_adamw_step with the reduce of zs_reduce_shard_ex:
  * the gradient is the grad_out value of zs_reduce_shard_ex for these
  * contributions and opts (never stored, scale included), then the AdamW
- * update of zs_adamw_step.
+ * update of zs_adamw_step; the working shard is stored as
+ * opts->working_shard_hint asks.
  * Arguments and errors as zs_adamw_step and zs_reduce_shard_ex.
  */
 zs_status zs_adamw_step_ex(float* p, float* m, float* v, uint16_t* w_out, int64_t S,

@@ -274,7 +274,16 @@ def test_hybrid_argument_errors(lib):
     for bad in (float("nan"), float("inf"), -float("inf")):
         assert step_scale(bad) == zs.ZS_EINVAL and "scale" in zs.zs_last_error()
         assert red_scale(bad) == zs.ZS_EINVAL and "scale" in zs.zs_last_error()
-    assert ctypes.sizeof(B.zs_reduce_opts) == 16      # int32, int32, double
+    assert ctypes.sizeof(B.zs_reduce_opts) == 24      # int32, int32, double, int32, int32
+
+    def step_hint(hint, reserved=0):
+        o = B.zs_reduce_opts(1, 0, 0.0, hint, reserved)
+        return lib.zs_adamw_step_ex(p, m, v, w, S, arr, 8, ctypes.byref(o), zs.ZS_BF16,
+                                    ctypes.byref(_hp()), None)
+
+    assert step_hint(2) == zs.ZS_EINVAL and "working_shard_hint" in zs.zs_last_error()
+    assert step_hint(-1) == zs.ZS_EINVAL
+    assert step_hint(zs.ZS_W_KEEP, reserved=1) == zs.ZS_EINVAL and "reserved" in zs.zs_last_error()
     assert step(8, 0, 0) == zs.ZS_EINVAL and "replicas" in zs.zs_last_error()
     assert step(8, 1, 2) == zs.ZS_EINVAL and "round_to_reduce_dtype" in zs.zs_last_error()
     assert step(8, 9, 0) == zs.ZS_EINVAL and "exceeds" in zs.zs_last_error()

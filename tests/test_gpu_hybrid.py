@@ -99,6 +99,32 @@ def test_adamw_ex_scale_matches_oracle(dtype, R, D, rnd, scale, offset):
     check_bf16(to_np(w), ow, what + " w", exact=True)
 
 
+@pytest.mark.parametrize("dtype", [O.BF16, O.FP32])
+@pytest.mark.parametrize("R,D,rnd", [(1, 8, False), (2, 4, True)])
+def test_keep_working_shard_hint_changes_no_bits(dtype, R, D, rnd):
+    """ZS_W_KEEP (cache-allocating stores of the working shard) gives the
+    same p, m, v and w as the default non-temporal stores, and the oracle's."""
+    dev = device()
+    S = 3 * 1024 * 8 + 19
+    a = state(S, 60 + R + D, dev)
+    b = [t.clone() for t in a]
+    op, om, ov = to_np(a[0]), np.zeros(S, np.float32), np.zeros(S, np.float32)
+    for t in (1, 2):
+        cs = contribs(R * D, S, dtype, 500 * t + R + D, dev)
+        hp = dict(step=t, **HP)
+        zs.zs_adamw_step_ex(*a, cs, hp, replicas=R, round_to_reduce_dtype=rnd)
+        zs.zs_adamw_step_ex(*b, cs, hp, replicas=R, round_to_reduce_dtype=rnd,
+                            keep_working_shard=True)
+        op, om, ov, ow = O.rank_step_hybrid(op, om, ov, [to_np(c) for c in cs], dtype,
+                                            O.AdamWHP(**hp), R, rnd)
+    torch.cuda.synchronize()
+    for x, y, name in zip(a, b, "pmvw"):
+        assert torch.equal(x.view(torch.int32) if x.dtype == torch.float32 else x,
+                           y.view(torch.int32) if y.dtype == torch.float32 else y), name
+    check_f32(to_np(b[0]), op, "keep p", exact=True)
+    check_bf16(to_np(b[3]), ow, "keep w", exact=True)
+
+
 def test_scale_zero_means_the_mean():
     """scale = 0 (the default) and scale = 1/(R*D) give the same bits."""
     dev = device()
