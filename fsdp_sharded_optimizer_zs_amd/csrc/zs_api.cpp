@@ -279,8 +279,8 @@ zs_status check_groups(const char* who, int32_t nd, const zs_reduce_opts* opts, 
             return fail(ZS_EINVAL, "%s: replicas = %d < 1", who, opts->replicas);
         if (opts->round_to_reduce_dtype != 0 && opts->round_to_reduce_dtype != 1)
             return fail(ZS_EINVAL, "%s: round_to_reduce_dtype must be 0 or 1", who);
-        if (!std::isfinite(opts->scale))
-            return fail(ZS_EINVAL, "%s: scale must be finite", who);
+        if (!std::isfinite(opts->scale) || !std::isfinite(float(opts->scale)))
+            return fail(ZS_EINVAL, "%s: scale must be finite (in fp32, once rounded)", who);
         *R = opts->replicas;
         *rnd = opts->round_to_reduce_dtype == 1;
         scale = opts->scale;

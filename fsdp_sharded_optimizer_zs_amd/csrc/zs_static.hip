@@ -49,8 +49,13 @@ hipError_t static_state(const StaticState** out) {
         if ((e = hipGetSymbolAddress(&fresh.ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
         if (fresh.ptr == nullptr || (reinterpret_cast<uintptr_t>(fresh.ptr) & 255) != 0)
             return hipErrorInvalidSymbol;
-        for (hipEvent_t& x : fresh.ev)
-            if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
+        for (hipEvent_t& x : fresh.ev) {
+            if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) {
+                for (hipEvent_t y : fresh.ev)
+                    if (y) (void)hipEventDestroy(y);
+                return e;
+            }
+        }
         st = fresh;
     }
     *out = &st;

@@ -225,9 +225,9 @@ typedef struct {
     int32_t replicas;               /* R >= 1 replica groups (HYBRID_SHARD nodes) */
     int32_t round_to_reduce_dtype;  /* 0 or 1: each collective's output is held
                                        in the reduce dtype                        */
-    double scale;                   /* finite; the one multiplier of the reduced
-                                       sum, rounded to fp32 once; 0 means
-                                       1 / (R * D)                                */
+    double scale;                   /* finite, and finite once rounded to fp32;
+                                       the one multiplier of the reduced sum,
+                                       rounded to fp32 once; 0 means 1 / (R * D)  */
     int32_t working_shard_hint;     /* ZS_W_STREAM or ZS_W_KEEP                   */
     int32_t reserved;               /* must be 0                                  */
 } zs_reduce_opts;

@@ -271,7 +271,7 @@ def test_hybrid_argument_errors(lib):
         o = B.zs_reduce_opts(2, 1, scale)
         return lib.zs_reduce_shard_ex(arr, 4, ctypes.byref(o), zs.ZS_BF16, S, A + 0x40000, None)
 
-    for bad in (float("nan"), float("inf"), -float("inf")):
+    for bad in (float("nan"), float("inf"), -float("inf"), 1e300, -3.5e38):
         assert step_scale(bad) == zs.ZS_EINVAL and "scale" in zs.zs_last_error()
         assert red_scale(bad) == zs.ZS_EINVAL and "scale" in zs.zs_last_error()
     assert ctypes.sizeof(B.zs_reduce_opts) == 24      # int32, int32, double, int32, int32
