@@ -158,6 +158,25 @@ def snapshot_step(zs, sl_tensors, cs, h, n=None, keep_working_shard=False):
     return snap, out
 
 
+def timed_calls(torch, fn, reps: int, warm: int = 3) -> float:
+    """Average ms per call of `reps` back-to-back calls of fn, timed with
+    events, after `warm` untimed calls queued just before them (no host
+    synchronization in between). The warm calls keep the GPU busy while the
+    host queues the timed ones, so that the events see only GPU time, and
+    take the first touches of the buffers: on the ragged unit the first few
+    packs after the inputs are made run about 10% slower than later ones."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    for _ in range(warm):
+        fn()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def pipeline_leg(zs, torch, p, m, v, wshard, buckets, pool, D, step_t, hp):
     """Per-bucket streamed step over all of the rank's buckets:
     contributions copied into two alternating staging slots on a transfer
@@ -370,9 +389,12 @@ def configs_leg(zs, torch, W, dev, hp, launches: int, arenas, oracle: bool):
         hps = [zs.AdamWHP(step=t, **hp) for t in range(2, 2 + launches)]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        # A long fill ahead of the launches keeps the GPU busy while the host
-        # queues them, so that small shards are timed back to back on the GPU
-        # rather than at the rate the host can issue calls.
+        # Two untimed launches, then a long fill ahead of the timed ones keeps
+        # the GPU busy while the host queues them, so that small shards are
+        # timed back to back on the GPU rather than at the rate the host can
+        # issue calls.
+        for h in hps[:2]:
+            zs.zs_adamw_step(p, m, v, ws, cs, h)
         busy.fill_(1.0)
         e0.record()
         for h in hps:
@@ -406,35 +428,15 @@ def ragged_move_leg(zs, torch, W, dev, reps: int = 5):
     unit = w.units[0]
     D = w.D
     res = {}
-    busy = torch.empty(1 << 30, device=dev)        # 4 GiB: a fill of about 0.6 ms
     for dtype in ("f32", "bf16"):
         ts = [t.reshape(-1) for t in W.tensor_values(unit, dtype, 5, dev)]
         _, N, N_pad, S = zs.zs_unit_layout(unit.numels, D)
         es = ts[0].element_size()
         shards = [torch.empty(S, dtype=ts[0].dtype, device=dev) for _ in range(D)]
         flat = torch.empty(N_pad, dtype=ts[0].dtype, device=dev)
-        table = zs.zs_pack_flat(ts, D, shards)               # warm, builds the table
-        zs.zs_gather_unit(shards, flat)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        torch.cuda.synchronize()
-        # GPU fills ahead of each timed group (about 2.4 ms) keep the GPU busy
-        # while the host queues the launches (each pack call checks the table
-        # of 10,000 tensors on the host), so that kernels are timed back to back
-        for _ in range(4):
-            busy.fill_(1.0)
-        e[0].record()
-        for _ in range(reps):
-            zs.zs_pack_flat(ts, D, shards, table=table)
-        e[1].record()
-        torch.cuda.synchronize()
-        for _ in range(4):
-            busy.fill_(1.0)
-        e[2].record()
-        for _ in range(reps):
-            zs.zs_gather_unit(shards, flat)
-        e[3].record()
-        torch.cuda.synchronize()
-        pack_ms, gather_ms = e[0].elapsed_time(e[1]) / reps, e[2].elapsed_time(e[3]) / reps
+        table = zs.zs_pack_flat(ts, D, shards)               # builds the table
+        pack_ms = timed_calls(torch, lambda: zs.zs_pack_flat(ts, D, shards, table=table), reps)
+        gather_ms = timed_calls(torch, lambda: zs.zs_gather_unit(shards, flat), reps)
         pos, exact = 0, True
         for t in ts:
             exact = exact and bool(torch.equal(flat[pos:pos + t.numel()], t))
@@ -449,8 +451,6 @@ def ragged_move_leg(zs, torch, W, dev, reps: int = 5):
             raise SystemExit(f"ragged {dtype}: gather(pack(x)) != x")
         del ts, shards, flat, table
         torch.cuda.empty_cache()
-    del busy
-    torch.cuda.empty_cache()
     return res
 
 
@@ -466,15 +466,7 @@ def reshard_ckpt_leg(zs, torch, W, dev, p, m, v, wshard, sl, D):
     S, S2 = -(-N // D), -(-N // 6)
     src = [p[sl][:S] for _ in range(1)] + [torch.empty(S, device=dev) for _ in range(D - 1)]
     dst = [torch.empty(S2, device=dev) for _ in range(6)]
-    zs.zs_reshard(src, N, dst)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(5):
-        zs.zs_reshard(src, N, dst)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 5
+    ms = timed_calls(torch, lambda: zs.zs_reshard(src, N, dst), 5)
     res = {"reshard_block_unit_f32_8_to_6": {"elements": N, "ms": ms,
                                               "GB_s": 8 * N / (ms / 1e3) / 1e9}}
     del src, dst
@@ -483,14 +475,7 @@ def reshard_ckpt_leg(zs, torch, W, dev, p, m, v, wshard, sl, D):
     # offset from its sources (the shifted-load path)
     src = [wshard[sl][:S]] + [torch.empty(S, dtype=torch.int16, device=dev) for _ in range(D - 1)]
     dst = [torch.empty(S2, dtype=torch.int16, device=dev) for _ in range(6)]
-    zs.zs_reshard(src, N, dst)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(5):
-        zs.zs_reshard(src, N, dst)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 5
+    ms = timed_calls(torch, lambda: zs.zs_reshard(src, N, dst), 5)
     res["reshard_block_unit_bf16_8_to_6"] = {"elements": N, "ms": ms,
                                              "GB_s": 4 * N / (ms / 1e3) / 1e9}
     del src, dst
@@ -706,15 +691,10 @@ def main() -> int:
     blk = w.units[0]
     ts = [t.reshape(-1) for t in W.tensor_values(blk, "f32", 1, dev)]
     bshards = [torch.empty(sizes[0], device=dev) for _ in range(D)]
-    zs.zs_pack_flat(ts, D, bshards)            # warm
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    zs.zs_pack_flat(ts, D, bshards)
-    e1.record()
-    torch.cuda.synchronize()
-    pack_ms = e0.elapsed_time(e1)
+    table = zs.zs_pack_flat(ts, D, bshards)
+    pack_ms = timed_calls(torch, lambda: zs.zs_pack_flat(ts, D, bshards, table=table), 5)
     pack_bytes = 2 * 4 * blk.numel
-    del ts, bshards
+    del ts, bshards, table
     torch.cuda.empty_cache()
 
     buckets = []
@@ -917,15 +897,8 @@ def main() -> int:
         a = torch.empty(1 << 30, device=dev)          # 4 GiB fp32
         bb = torch.empty_like(a)
         a.fill_(1.0)
-        bb.copy_(a)                                   # warm
-        torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record()
-        bb.copy_(a)
-        c1.record()
-        torch.cuda.synchronize()
-        out["copy_4GiB"] = {"ms": c0.elapsed_time(c1),
-                            "GB_s": 2 * 4 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9}
+        copy_ms = timed_calls(torch, lambda: bb.copy_(a), 4, warm=2)
+        out["copy_4GiB"] = {"ms": copy_ms, "GB_s": 2 * 4 * (1 << 30) / (copy_ms / 1e3) / 1e9}
         del a, bb
     if not args.no_unfused:
         log("unfused leg: zs_reduce_shard then zs_adamw_step on the same buckets")

@@ -34,6 +34,33 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 static_assert(sizeof(u32x4_a4) == 16, "a 4-aligned vector keeps 16-byte steps");
 
+// Sources are read through global-address-space pointers. A source address
+// that passes through an integer (the alignment tests below) or through
+// memory (the pack table) is otherwise a generic pointer, read with flat_load
+// instructions, which also count against the LDS/scalar-load counter, so
+// that a wait for a table read or a lane exchange waits for the copy loads in
+// flight too. Every pointer here is device or pinned memory, never LDS or
+// private memory, so the global forms are valid. (Measured on the same
+// buffers, the ragged and 70B block units pack and re-shard at the same rate
+// either way.) The source vector type for an alignment is a member typedef:
+// as a template argument, a typedef loses its 4-byte alignment, and the
+// compiler would take a 4-byte aligned source as 16-byte aligned.
+#define ZS_GLOBAL __attribute__((address_space(1)))
+typedef ZS_GLOBAL const u32x4 g_u32x4;        // 16-byte aligned source vector
+typedef ZS_GLOBAL const u32x4_a4 g_u32x4_a4;  // 4-byte aligned source vector
+typedef ZS_GLOBAL const uint32_t g_u32;
+typedef ZS_GLOBAL const uint16_t g_u16;
+template <int A>
+struct SrcVec;
+template <>
+struct SrcVec<16> {
+    typedef g_u32x4 T;
+};
+template <>
+struct SrcVec<4> {
+    typedef g_u32x4_a4 T;
+};
+
 constexpr int kThreads = 256;
 // Pack and re-shard work items are 8 KiB of destination: 512 aligned 16-byte
 // vectors, two per lane of a 256-thread workgroup, both loads in flight
@@ -53,18 +80,22 @@ struct Elem;
 template <>
 struct Elem<2> {
     using T = uint16_t;
+    typedef g_u16 G;
 };
 template <>
 struct Elem<4> {
     using T = uint32_t;
+    typedef g_u32 G;
 };
 
-// Body vectors i = tid, tid + nthr, ... < body from source vectors of type V
-// (16 bytes at 16- or 4-byte alignment) to 16-byte aligned destination
+// Body vectors i = tid, tid + nthr, ... < body from 16-byte source vectors
+// at address sa, aligned to A (16 or 4) bytes, to 16-byte aligned destination
 // vectors, kUnroll loads in flight per lane before their stores.
-template <typename V>
-__device__ __forceinline__ void copy_vecs(u32x4* __restrict__ db, const V* __restrict__ s4,
-                                          int64_t body, int64_t tid, int64_t nthr) {
+template <int A>
+__device__ __forceinline__ void copy_vecs(u32x4* __restrict__ db, uintptr_t sa, int64_t body,
+                                          int64_t tid, int64_t nthr) {
+    typedef typename SrcVec<A>::T V;
+    const V* __restrict__ s4 = reinterpret_cast<const V*>(sa);
     int64_t i = tid;
     for (; i + (kUnroll - 1) * nthr < body; i += kUnroll * nthr) {
         u32x4 x[kUnroll];
@@ -94,7 +125,7 @@ __device__ __forceinline__ void copy_vecs(u32x4* __restrict__ db, const V* __res
 // 5-8% slower.
 template <int W>
 __device__ __forceinline__ void copy_vecs_odd(u32x4* __restrict__ db,
-                                              const u32x4* __restrict__ a4, int64_t body,
+                                              const g_u32x4* __restrict__ a4, int64_t body,
                                               int64_t tid, int64_t nthr) {
     const int lane = int(tid & 63);
     for (int64_t i0 = tid - lane; i0 < body; i0 += kUnroll * nthr) {
@@ -141,27 +172,29 @@ template <int ES>
 __device__ __forceinline__ void copy_run(char* dst, const char* src, int64_t n, int64_t tid,
                                          int64_t nthr) {
     using T = typename Elem<ES>::T;
+    typedef typename Elem<ES>::G G;
     constexpr int V = 16 / ES;
     int64_t head = int64_t((16 - (reinterpret_cast<uintptr_t>(dst) & 15)) & 15) / ES;
     if (head > n) head = n;
     const int64_t body = (n - head) / V;
     const int64_t tail = n - head - body * V;
+    const G* gs = reinterpret_cast<const G*>(reinterpret_cast<uintptr_t>(src));
     if (tid < head) {
-        reinterpret_cast<T*>(dst)[tid] = reinterpret_cast<const T*>(src)[tid];
+        reinterpret_cast<T*>(dst)[tid] = gs[tid];
     } else if (tid - head < tail) {
         const int64_t e = head + body * V + (tid - head);
-        reinterpret_cast<T*>(dst)[e] = reinterpret_cast<const T*>(src)[e];
+        reinterpret_cast<T*>(dst)[e] = gs[e];
     }
     if (body <= 0) return;
     u32x4* db = reinterpret_cast<u32x4*>(dst + head * ES);
     const uintptr_t sa = reinterpret_cast<uintptr_t>(src + head * ES);
     if ((sa & 15) == 0) {
-        copy_vecs(db, reinterpret_cast<const u32x4*>(sa), body, tid, nthr);
+        copy_vecs<16>(db, sa, body, tid, nthr);
     } else if ((sa & 3) == 0) {
         // a dword-aligned source still loads as one dwordx4 per vector
-        copy_vecs(db, reinterpret_cast<const u32x4_a4*>(sa), body, tid, nthr);
+        copy_vecs<4>(db, sa, body, tid, nthr);
     } else {  // 2-byte elements at an odd element offset
-        const u32x4* a4 = reinterpret_cast<const u32x4*>(sa & ~uintptr_t(15));
+        const g_u32x4* a4 = reinterpret_cast<const g_u32x4*>(sa & ~uintptr_t(15));
         switch ((sa & 15) >> 2) {  // the same for every lane of the run
             case 0: copy_vecs_odd<0>(db, a4, body, tid, nthr); break;
             case 1: copy_vecs_odd<1>(db, a4, body, tid, nthr); break;

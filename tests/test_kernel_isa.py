@@ -14,6 +14,10 @@ cross-compiles).
   and two-level, fused and reduce-only) issue their contribution loads in
   batches before waiting: an unrolled 16-way fold once issued them one at a
   time behind waits (5.1 against 6.2 TB/s).
+- Every kernel reads device memory with global (or scalar) loads, never flat
+  ones, and the sources compile without an alignment-mismatch warning (a
+  4-byte aligned source vector once reached the copy loop typed as 16-byte
+  aligned).
 """
 import os
 import re
@@ -35,6 +39,7 @@ def asm(tmp_path_factory):
     if HIPCC is None:
         pytest.skip("hipcc not available")
     out = {}
+    warnings = {}
     d = tmp_path_factory.mktemp("isa")
     flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC")]
     for src in ("zs_step.hip", "zs_move.hip", "zs_diag.hip"):
@@ -44,6 +49,8 @@ def asm(tmp_path_factory):
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
         out[src] = dst.read_text()
+        warnings[src] = r.stderr
+    out["warnings"] = warnings
     return out
 
 
@@ -58,6 +65,8 @@ def functions(text):
 
 def test_no_packed_fp32_instructions(asm):
     for src, text in asm.items():
+        if src == "warnings":
+            continue
         hits = re.findall(r"^\s*(v_pk_(?:add|mul|fma)_f32)\b", text, re.M)
         assert not hits, f"{src}: {sorted(set(hits))}"
 
@@ -108,3 +117,11 @@ def test_long_bf16_folds_issue_loads_in_batches(asm):
         runs = load_runs(b)
         singles = sum(1 for r in runs if r == 1)
         assert 10 * singles <= sum(runs), f"{n}: load runs {runs}"
+
+
+def test_kernels_use_global_loads_and_true_alignment(asm):
+    for src in ("zs_step.hip", "zs_move.hip", "zs_diag.hip"):
+        for n, b in functions(asm[src]):
+            flat = re.findall(r"^\s*(flat_(?:load|store)\w*)", b, re.M)
+            assert not flat, f"{src} {n}: {sorted(set(flat))}"
+        assert "align-mismatch" not in asm["warnings"][src], asm["warnings"][src][-2000:]
