@@ -341,7 +341,9 @@ typedef struct {
  *                this call has completed, every copy has completed too
  *   transfer     stream that runs the copies (may equal compute: no overlap)
  * Returns after enqueuing; nothing is synchronized and no device memory is
- * allocated (five events are created and released per call).
+ * allocated. The five events that order the two streams come from a
+ * per-device pool in the library (created on first use, reused by later
+ * calls), so a call creates no runtime object once the pool holds them.
  * Errors: ZS_EINVAL (NULLs, misalignment, a bucket larger than staging_len,
  * hyperparameters), ZS_EALIAS (any two of the buckets' p, m, v, w_out and the
  * staging slots overlap, or a source overlaps one of them), ZS_EUNSUPPORTED,
