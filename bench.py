@@ -722,42 +722,51 @@ def main() -> int:
 
     n_launch = len(buckets)
     K = args.steps
-    # one event triple per (timed step, bucket), read only after the timed region
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_launch)]
+    # Per (timed step, bucket), two events that the fused kernel's launch
+    # itself records at the kernel's start and end (zs_adamw_step_timed: the
+    # kernel's own execution time, with no marker packets enqueued between the
+    # kernels), and per timed step one event after its last gather; all read
+    # only after the timed region. Recording each once here creates it.
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_launch)]
           for _ in range(K)]
+    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for e in [x for evs in ev for pair in evs for x in pair] + ev_end:
+        e.record()
+    torch.cuda.synchronize()
 
     # Each unit's fused step is followed at once by its all-gather, which reads
     # the rank's fresh working shard: the step stores that shard with
     # cache-allocating stores (ZS_W_KEEP), so the gather reads it from the
     # Infinity Cache and it crosses HBM once (written back later) instead of
     # twice. Every other stream stays non-temporal; the bits are the same.
-    def fused(sl, cs, h):
-        zs.zs_adamw_step_ex(p[sl], m[sl], v[sl], wshard[sl], cs, h, keep_working_shard=True)
-
-    def step(t: int, evs):
+    def step(t: int, evs, end):
         h = zs.AdamWHP(step=t, **hp)
         for i, (sl, sz, cs, shards, ubuf) in enumerate(buckets):
             if evs:
-                evs[i][0].record()
-            fused(sl, cs, h)
-            if evs:
-                evs[i][1].record()
+                zs.zs_adamw_step_timed(p[sl], m[sl], v[sl], wshard[sl], cs, h, evs[i][0],
+                                       evs[i][1], keep_working_shard=True)
+            else:
+                zs.zs_adamw_step_ex(p[sl], m[sl], v[sl], wshard[sl], cs, h,
+                                    keep_working_shard=True)
             zs.zs_gather_unit(shards, ubuf)
-            if evs:
-                evs[i][2].record()
+        if end is not None:
+            end.record()
 
     log(f"warmup {args.warmup} step(s)")
     for t in range(1, args.warmup + 1):
-        step(t, None)
+        step(t, None, None)
     torch.cuda.synchronize()
     log(f"timing {K} step(s) of {n_launch} units")
     t0 = time.perf_counter()
     for j in range(K):
-        step(args.warmup + 1 + j, ev[j])
+        step(args.warmup + 1 + j, ev[j], ev_end[j])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     adam_ms = sum(e[0].elapsed_time(e[1]) for evs in ev for e in evs)
-    gather_ms = sum(e[1].elapsed_time(e[2]) for evs in ev for e in evs)
+    # each gather: from its unit's fused kernel's end to the next one's start
+    # (after the last unit, to the step's end event)
+    gather_ms = sum(evs[i][1].elapsed_time(evs[i + 1][0] if i + 1 < n_launch else ev_end[j])
+                    for j, evs in enumerate(ev) for i in range(n_launch))
     ms_per_step = elapsed * 1e3 / K
     log(f"{ms_per_step:.2f} ms/step")
 
@@ -800,25 +809,28 @@ def main() -> int:
         # the fused kernel alone over the same buckets (no gathers between,
         # the working shard stored non-temporally like every other stream):
         # the like-for-like partner of the stream ceiling
+        # (both timed like the main leg: events tied to each kernel launch)
         fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_launch)]
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_launch)]
+        for e in [x for pair in fev + cev for x in pair]:
+            e.record()
         for rep in range(2):
             h = zs.AdamWHP(step=args.warmup + K + 2 + rep, **hp)
             for i, (sl, sz, cs, _, _) in enumerate(buckets):
                 if rep:
-                    fev[i][0].record()
-                zs.zs_adamw_step(p[sl], m[sl], v[sl], wshard[sl], cs, h)
-                if rep:
-                    fev[i][1].record()
+                    zs.zs_adamw_step_timed(p[sl], m[sl], v[sl], wshard[sl], cs, h, fev[i][0],
+                                           fev[i][1])
+                else:
+                    zs.zs_adamw_step(p[sl], m[sl], v[sl], wshard[sl], cs, h)
         torch.cuda.synchronize()
         alone_s = sum(a.elapsed_time(b) for a, b in fev) / 1e3 / n_launch
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_launch)]
         for rep in range(2):
             for i, (sl, sz, cs, _, _) in enumerate(buckets):
                 if rep:
-                    cev[i][0].record()
-                zs.zs_stream_ceiling(p[sl], m[sl], v[sl], wshard[sl], cs)
-                if rep:
-                    cev[i][1].record()
+                    zs.zs_stream_ceiling_timed(p[sl], m[sl], v[sl], wshard[sl], cs, cev[i][0],
+                                               cev[i][1])
+                else:
+                    zs.zs_stream_ceiling(p[sl], m[sl], v[sl], wshard[sl], cs)
         torch.cuda.synchronize()
         ceiling_s = sum(a.elapsed_time(b) for a, b in cev) / 1e3 / n_launch
         for a in range(0, S, 1 << 30):
@@ -891,6 +903,9 @@ def main() -> int:
             "algorithmic_bytes_per_param": bpp,
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "avg_launch_ms": adam_avg_s * 1e3,
+            "launch_timing": "HIP events recorded by each fused kernel's launch at the kernel's "
+                             "own start and end (zs_adamw_step_timed, hipExtLaunchKernel) on its "
+                             "stream; the stream ceiling and fused_alone are timed the same way",
             "median_launch_GB_s": median_rate,
             "stream_ceiling": ceiling,
         },

@@ -13,14 +13,15 @@ from ._binding import (  # noqa: F401
     zs_unit_layout, zs_reshard, zs_shard_save, zs_shard_info_read, zs_shard_load,
     zs_shard_load_resharded, ZS_EIO, zs_adamw_step_host, zs_offload_step, zs_stream_ceiling,
     zs_hbm_probe, ZS_PROBE_READ, ZS_PROBE_WRITE, ZS_PROBE_COPY, ZS_PROBE_TRIAD, PackTable,
-    zs_step_pipelined_static, ZS_W_STREAM, ZS_W_KEEP,
+    zs_step_pipelined_static, ZS_W_STREAM, ZS_W_KEEP, zs_adamw_step_timed,
+    zs_stream_ceiling_timed,
 )
 
 __all__ = [
     "zs_unit_layout", "zs_pack_flat", "zs_reduce_shard", "zs_adamw_step",
-    "zs_reduce_shard_ex", "zs_adamw_step_ex", "zs_reshard", "zs_shard_save",
-    "zs_shard_info_read", "zs_shard_load", "zs_shard_load_resharded", "zs_adamw_step_host",
-    "zs_offload_step", "zs_stream_ceiling", "zs_hbm_probe",
+    "zs_reduce_shard_ex", "zs_adamw_step_ex", "zs_adamw_step_timed", "zs_reshard",
+    "zs_shard_save", "zs_shard_info_read", "zs_shard_load", "zs_shard_load_resharded", "zs_adamw_step_host",
+    "zs_offload_step", "zs_stream_ceiling", "zs_stream_ceiling_timed", "zs_hbm_probe",
     "ZS_PROBE_READ", "ZS_PROBE_WRITE", "ZS_PROBE_COPY", "ZS_PROBE_TRIAD",
     "zs_gather_unit", "zs_step_pipelined", "zs_last_error", "zs_abi_version", "AdamWHP", "ZsError",
     "ZS_BF16", "ZS_F32", "ZS_MAX_D", "load", "PackTable", "zs_step_pipelined_static",

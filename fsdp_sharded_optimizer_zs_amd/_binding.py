@@ -98,10 +98,15 @@ def load() -> ctypes.CDLL:
                 "zs_reduce_shard_ex": (i32, [P(vp), i32, P(zs_reduce_opts), i32, i64, vp, vp]),
                 "zs_adamw_step_ex": (i32, [vp, vp, vp, vp, i64, P(vp), i32, P(zs_reduce_opts),
                                            i32, P(zs_adamw_hp), vp]),
+                "zs_adamw_step_timed": (i32, [vp, vp, vp, vp, i64, P(vp), i32,
+                                              P(zs_reduce_opts), i32, P(zs_adamw_hp), vp, vp,
+                                              vp]),
                 "zs_gather_unit": (i32, [P(vp), i32, i64, i32, vp, vp]),
                 "zs_reshard": (i32, [P(vp), i32, i64, i64, i32, P(vp), i32, i64, vp]),
                 "zs_adamw_step_host": (i32, [vp, vp, vp, vp, i64, vp, P(zs_adamw_hp), i32]),
                 "zs_stream_ceiling": (i32, [vp, vp, vp, vp, i64, P(vp), i32, i32, vp]),
+                "zs_stream_ceiling_timed": (i32, [vp, vp, vp, vp, i64, P(vp), i32, i32, vp, vp,
+                                                  vp]),
                 "zs_hbm_probe": (i32, [i32, vp, vp, i64, i32, vp]),
                 "zs_offload_step": (i32, [P(vp), i32, i32, i64, vp, vp, vp, vp, vp, vp, vp,
                                           P(zs_adamw_hp), i32, i64, vp, vp]),
@@ -347,12 +352,10 @@ def zs_reduce_shard_ex(contribs: Sequence, grad_out, replicas: int = 1,
                                      _stream(grad_out, stream)))
 
 
-def zs_adamw_step_ex(p, m, v, w_out, contribs: Sequence, hp, replicas: int = 1,
-                     round_to_reduce_dtype: bool = False, stream=None,
-                     scale: float = 0.0, keep_working_shard: bool = False) -> None:
-    """zs_adamw_step with the reduce of zs_reduce_shard_ex; keep_working_shard
-    stores the bf16 working shard with cache-allocating stores, for a caller
-    that reads it right after (the unit's all-gather)."""
+def _adamw_ex_args(p, m, v, w_out, contribs, hp, replicas, round_to_reduce_dtype, scale,
+                   keep_working_shard):
+    """Checked arguments of zs_adamw_step_ex / _timed, up to opts and hp
+    (kept alive by the returned tuple)."""
     torch = _torch()
     S = p.numel()
     for name, t in (("p", p), ("m", m), ("v", v)):
@@ -371,10 +374,46 @@ def zs_adamw_step_ex(p, m, v, w_out, contribs: Sequence, hp, replicas: int = 1,
     opts = zs_reduce_opts(int(replicas), 1 if round_to_reduce_dtype else 0, float(scale),
                           ZS_W_KEEP if keep_working_shard else ZS_W_STREAM, 0)
     h = _hp(hp)
-    _check(load().zs_adamw_step_ex(ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(m.data_ptr()),
-                                   ctypes.c_void_p(v.data_ptr()),
-                                   ctypes.c_void_p(w_out.data_ptr()), S, _ptr_array(contribs), D,
-                                   ctypes.byref(opts), code, ctypes.byref(h), _stream(p, stream)))
+    return (ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(m.data_ptr()),
+            ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(w_out.data_ptr()), S,
+            _ptr_array(contribs), D, opts, code, h)
+
+
+def zs_adamw_step_ex(p, m, v, w_out, contribs: Sequence, hp, replicas: int = 1,
+                     round_to_reduce_dtype: bool = False, stream=None,
+                     scale: float = 0.0, keep_working_shard: bool = False) -> None:
+    """zs_adamw_step with the reduce of zs_reduce_shard_ex; keep_working_shard
+    stores the bf16 working shard with cache-allocating stores, for a caller
+    that reads it right after (the unit's all-gather)."""
+    pp, mp, vp_, wp, S, arr, D, opts, code, h = _adamw_ex_args(
+        p, m, v, w_out, contribs, hp, replicas, round_to_reduce_dtype, scale, keep_working_shard)
+    _check(load().zs_adamw_step_ex(pp, mp, vp_, wp, S, arr, D, ctypes.byref(opts), code,
+                                   ctypes.byref(h), _stream(p, stream)))
+
+
+def _event_handle(e, name):
+    if isinstance(e, int):
+        handle = e
+    else:
+        handle = int(getattr(e, "cuda_event", 0) or 0)   # torch.cuda.Event
+    if not handle:
+        raise ValueError(f"{name}: a created event is needed (a torch.cuda.Event with "
+                         "enable_timing=True exists once it has been recorded)")
+    return ctypes.c_void_p(handle)
+
+
+def zs_adamw_step_timed(p, m, v, w_out, contribs: Sequence, hp, start, stop, replicas: int = 1,
+                        round_to_reduce_dtype: bool = False, stream=None, scale: float = 0.0,
+                        keep_working_shard: bool = False) -> None:
+    """zs_adamw_step_ex whose kernel records `start` and `stop` (timing events:
+    torch.cuda.Event(enable_timing=True), recorded once beforehand so that
+    they exist, or raw hipEvent_t handles) at its own start and end; then
+    start.elapsed_time(stop) is the kernel's execution time."""
+    pp, mp, vp_, wp, S, arr, D, opts, code, h = _adamw_ex_args(
+        p, m, v, w_out, contribs, hp, replicas, round_to_reduce_dtype, scale, keep_working_shard)
+    _check(load().zs_adamw_step_timed(pp, mp, vp_, wp, S, arr, D, ctypes.byref(opts), code,
+                                      ctypes.byref(h), _event_handle(start, "start"),
+                                      _event_handle(stop, "stop"), _stream(p, stream)))
 
 
 def zs_gather_unit(shards: Sequence, flat_out, stream=None) -> None:
@@ -579,9 +618,7 @@ def zs_offload_step(contribs: Sequence, grad_dev, grad_host, p, m, v, w_host, w_
         _stream(grad_dev, h2d_stream)))
 
 
-def zs_stream_ceiling(p, m, v, w, contribs: Sequence, stream=None) -> None:
-    """Measurement aid: the fused step's streams without its arithmetic
-    (p, m, v, w are overwritten with placeholders)."""
+def _ceiling_args(p, m, v, w, contribs):
     S = p.numel()
     ptrs = _state(p, m, v, w)
     code = _dtype_code(contribs[0])
@@ -589,8 +626,22 @@ def zs_stream_ceiling(p, m, v, w, contribs: Sequence, stream=None) -> None:
         _dev(c, f"contribs[{i}]")
         if c.numel() != S or _dtype_code(c) != code:
             raise ValueError("contributions must share one dtype and hold S elements")
-    _check(load().zs_stream_ceiling(*ptrs, S, _ptr_array(contribs), len(contribs), code,
-                                    _stream(p, stream)))
+    return ptrs, S, _ptr_array(contribs), len(contribs), code
+
+
+def zs_stream_ceiling(p, m, v, w, contribs: Sequence, stream=None) -> None:
+    """Measurement aid: the fused step's streams without its arithmetic
+    (p, m, v, w are overwritten with placeholders)."""
+    ptrs, S, arr, n, code = _ceiling_args(p, m, v, w, contribs)
+    _check(load().zs_stream_ceiling(*ptrs, S, arr, n, code, _stream(p, stream)))
+
+
+def zs_stream_ceiling_timed(p, m, v, w, contribs: Sequence, start, stop, stream=None) -> None:
+    """zs_stream_ceiling whose kernel records `start` and `stop` (as for
+    zs_adamw_step_timed) at its own start and end."""
+    ptrs, S, arr, n, code = _ceiling_args(p, m, v, w, contribs)
+    _check(load().zs_stream_ceiling_timed(*ptrs, S, arr, n, code, _event_handle(start, "start"),
+                                          _event_handle(stop, "stop"), _stream(p, stream)))
 
 
 ZS_PROBE_READ, ZS_PROBE_WRITE, ZS_PROBE_COPY, ZS_PROBE_TRIAD = 0, 1, 2, 3

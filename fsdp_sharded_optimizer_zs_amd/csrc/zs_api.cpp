@@ -181,7 +181,7 @@ using namespace zs;
 
 ZS_EXPORT const char* zs_last_error(void) { return g_last_error.c_str(); }
 
-ZS_EXPORT int32_t zs_abi_version(void) { return 200; }
+ZS_EXPORT int32_t zs_abi_version(void) { return 201; }
 
 ZS_EXPORT zs_status zs_unit_layout(const int64_t* numels, int32_t T, int32_t D,
                                    int64_t* offsets_out, int64_t* n_out, int64_t* n_pad_out,
@@ -325,7 +325,8 @@ zs_status reduce_common(const char* who, const void* const* contribs, int32_t nd
 
 zs_status adamw_common(const char* who, float* p, float* m, float* v, uint16_t* w_out, int64_t S,
                        const void* const* contribs, int32_t nd, const zs_reduce_opts* opts,
-                       int32_t dtype, const zs_adamw_hp* hp, hipStream_t stream) {
+                       int32_t dtype, const zs_adamw_hp* hp, hipStream_t stream,
+                       hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
     const int es = elem_size(dtype);
     if (es == 0) return fail(ZS_EUNSUPPORTED, "%s: unknown dtype %d", who, dtype);
     int R;
@@ -363,7 +364,9 @@ zs_status adamw_common(const char* who, float* p, float* m, float* v, uint16_t* 
     AdamConsts k = adam_consts(*hp, n);
     k.inv_n = inv_n;
     k.keep_w = keep_w;
-    return hip_status(launch_adamw(p, m, v, w_out, S, cp, nd, R, rnd, dtype, k, al, stream), who);
+    return hip_status(
+        launch_adamw(p, m, v, w_out, S, cp, nd, R, rnd, dtype, k, al, stream, ev_start, ev_stop),
+        who);
 }
 
 }  // namespace
@@ -392,6 +395,18 @@ ZS_EXPORT zs_status zs_adamw_step_ex(float* p, float* m, float* v, uint16_t* w_o
                                      const zs_adamw_hp* hp, hipStream_t stream) {
     return adamw_common("zs_adamw_step_ex", p, m, v, w_out, S, contribs, D, opts, dtype, hp,
                         stream);
+}
+
+ZS_EXPORT zs_status zs_adamw_step_timed(float* p, float* m, float* v, uint16_t* w_out, int64_t S,
+                                        const void* const* contribs, int32_t D,
+                                        const zs_reduce_opts* opts, int32_t dtype,
+                                        const zs_adamw_hp* hp, hipEvent_t start, hipEvent_t stop,
+                                        hipStream_t stream) {
+    const char* who = "zs_adamw_step_timed";
+    if (start == nullptr || stop == nullptr)
+        return fail(ZS_EINVAL, "%s: start or stop event is NULL", who);
+    if (start == stop) return fail(ZS_EINVAL, "%s: start and stop are the same event", who);
+    return adamw_common(who, p, m, v, w_out, S, contribs, D, opts, dtype, hp, stream, start, stop);
 }
 
 ZS_EXPORT zs_status zs_gather_unit(const void* const* shards, int32_t D, int64_t S,
@@ -459,10 +474,11 @@ ZS_EXPORT zs_status zs_reshard(const void* const* src, int32_t D, int64_t S, int
     return hip_status(launch_reshard(sp, S, dp, D2, S2, N, es, stream), "zs_reshard launch");
 }
 
-ZS_EXPORT zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w, int64_t S,
-                                      const void* const* contribs, int32_t n, int32_t dtype,
-                                      hipStream_t stream) {
-    const char* who = "zs_stream_ceiling";
+namespace {
+
+zs_status ceiling_common(const char* who, float* p, float* m, float* v, uint16_t* w, int64_t S,
+                         const void* const* contribs, int32_t n, int32_t dtype, hipStream_t stream,
+                         hipEvent_t ev_start, hipEvent_t ev_stop) {
     const int es = elem_size(dtype);
     if (es == 0) return fail(ZS_EUNSUPPORTED, "%s: unknown dtype %d", who, dtype);
     if (n < 1 || n > ZS_MAX_D) return fail(ZS_EINVAL, "%s: n = %d outside 1..%d", who, n, ZS_MAX_D);
@@ -482,7 +498,27 @@ ZS_EXPORT zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w,
             if (overlap(rs[a], range_of(cp.p[q], S, es)))
                 return fail(ZS_EALIAS, "%s: contribution %d overlaps an output", who, q);
     }
-    return hip_status(launch_streams(p, m, v, w, S, cp, n, dtype, stream), who);
+    return hip_status(launch_streams(p, m, v, w, S, cp, n, dtype, stream, ev_start, ev_stop), who);
+}
+
+}  // namespace
+
+ZS_EXPORT zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w, int64_t S,
+                                      const void* const* contribs, int32_t n, int32_t dtype,
+                                      hipStream_t stream) {
+    return ceiling_common("zs_stream_ceiling", p, m, v, w, S, contribs, n, dtype, stream, nullptr,
+                          nullptr);
+}
+
+ZS_EXPORT zs_status zs_stream_ceiling_timed(float* p, float* m, float* v, uint16_t* w, int64_t S,
+                                            const void* const* contribs, int32_t n,
+                                            int32_t dtype, hipEvent_t start, hipEvent_t stop,
+                                            hipStream_t stream) {
+    const char* who = "zs_stream_ceiling_timed";
+    if (start == nullptr || stop == nullptr)
+        return fail(ZS_EINVAL, "%s: start or stop event is NULL", who);
+    if (start == stop) return fail(ZS_EINVAL, "%s: start and stop are the same event", who);
+    return ceiling_common(who, p, m, v, w, S, contribs, n, dtype, stream, start, stop);
 }
 
 ZS_EXPORT zs_status zs_hbm_probe(int32_t kind, void* buf, void* buf2, int64_t bytes,

@@ -14,6 +14,8 @@
 // into w the first two words of each 16-byte XOR of the contributions (bf16:
 // taken after the LDS exchange, the odd entries with 1 XORed into every word).
 
+#include <hip/hip_ext.h>
+
 #include "zs_internal.h"
 
 namespace zs {
@@ -179,15 +181,24 @@ __global__ __launch_bounds__(kThreads) void probe_triad_kernel(const u32x4* __re
 }  // namespace
 
 hipError_t launch_streams(float* p, float* m, float* v, uint16_t* w, int64_t S,
-                          const PtrPack& contribs, int n, int dtype, hipStream_t stream) {
+                          const PtrPack& contribs, int n, int dtype, hipStream_t stream,
+                          hipEvent_t ev_start, hipEvent_t ev_stop) {
     const int64_t npairs = S / (kPair * kTile);
-    const int64_t blocks = streams_grid(S, kPair);
-    if (dtype == ZS_BF16)
-        hipLaunchKernelGGL((streams_kernel<true>), dim3(unsigned(blocks)), dim3(kThreads), 0,
-                           stream, p, m, v, w, npairs, contribs, n);
-    else
-        hipLaunchKernelGGL((streams_kernel<false>), dim3(unsigned(blocks)), dim3(kThreads), 0,
-                           stream, p, m, v, w, npairs, contribs, n);
+    const dim3 grid{unsigned(streams_grid(S, kPair))}, block{unsigned(kThreads)};
+    if (ev_start != nullptr) {  // the events tied to this dispatch's start and end
+        if (dtype == ZS_BF16)
+            hipExtLaunchKernelGGL((streams_kernel<true>), grid, block, 0, stream, ev_start,
+                                  ev_stop, 0, p, m, v, w, npairs, contribs, n);
+        else
+            hipExtLaunchKernelGGL((streams_kernel<false>), grid, block, 0, stream, ev_start,
+                                  ev_stop, 0, p, m, v, w, npairs, contribs, n);
+    } else if (dtype == ZS_BF16) {
+        hipLaunchKernelGGL((streams_kernel<true>), grid, block, 0, stream, p, m, v, w, npairs,
+                           contribs, n);
+    } else {
+        hipLaunchKernelGGL((streams_kernel<false>), grid, block, 0, stream, p, m, v, w, npairs,
+                           contribs, n);
+    }
     return hipGetLastError();
 }
 

@@ -103,10 +103,13 @@ const DeviceInfo& device_info();
 
 // Kernel launchers (enqueue only; return the launch status). The reduce of
 // the step folds R groups of nd contributions (replica-major; R = 1 is the
-// flat fold), rounding each level to the reduce dtype when rnd is set.
+// flat fold), rounding each level to the reduce dtype when rnd is set. With
+// ev_start and ev_stop, the step's one kernel launch records them at its own
+// start and end (hipExtLaunchKernel) instead of a plain launch.
 hipError_t launch_adamw(float* p, float* m, float* v, uint16_t* w, int64_t S,
                         const PtrPack& contribs, int nd, int R, bool rnd, int dtype,
-                        const AdamConsts& k, bool aligned, hipStream_t stream);
+                        const AdamConsts& k, bool aligned, hipStream_t stream,
+                        hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_reduce(const PtrPack& contribs, int nd, int R, bool rnd, int dtype, int64_t S,
                          float inv_n, float* out, bool aligned, hipStream_t stream);
 hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es,
@@ -115,7 +118,8 @@ hipError_t launch_pack(const zs_tensor_ref* d_table, int T, int64_t N, int es,
 hipError_t launch_gather(const PtrPack& shards, int D, int64_t S, int es, void* flat,
                          uint64_t in_place, hipStream_t stream);
 hipError_t launch_streams(float* p, float* m, float* v, uint16_t* w, int64_t S,
-                          const PtrPack& contribs, int n, int dtype, hipStream_t stream);
+                          const PtrPack& contribs, int n, int dtype, hipStream_t stream,
+                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_probe(int kind, void* buf, void* buf2, int64_t nvec, int per_cu,
                         hipStream_t stream);
 hipError_t launch_reshard(const PtrPack& src, int64_t S, const PtrPack& dst, int D2, int64_t S2,

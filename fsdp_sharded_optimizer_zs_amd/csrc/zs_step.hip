@@ -30,6 +30,8 @@
 // below), division and sqrt are the correctly rounded IEEE operations, and
 // fp32 denormals are kept.
 
+#include <hip/hip_ext.h>
+
 #include "zs_internal.h"
 
 #pragma clang fp contract(off)
@@ -524,6 +526,8 @@ struct Job {
     int64_t S;
     AdamConsts k;
     bool aligned;
+    hipEvent_t ev_start;  // with ev_stop: recorded at the step kernel's own start and end
+    hipEvent_t ev_stop;
 };
 
 template <int DT, class Sum>
@@ -532,7 +536,18 @@ hipError_t launch_job(const Job& j, const PtrPack& c, const Sum& sum, hipStream_
     static_assert(kThreads == kBlockThreads, "grid arithmetic assumes 256-thread workgroups");
     const unsigned tiled = unsigned(step_tiled_grid(j.S, TP));
     const unsigned scalar = unsigned(step_scalar_grid(j.S));
-    if (j.out == nullptr) {
+    if (j.out == nullptr && j.ev_start != nullptr) {
+        // timed: the runtime ties the two events to this dispatch's start and
+        // end timestamps, with no marker packets around it
+        if (j.aligned)
+            hipExtLaunchKernelGGL((adamw_vec_kernel<DT, Sum, TP>), dim3(tiled), dim3(kThreads), 0,
+                                  stream, j.ev_start, j.ev_stop, 0, j.p, j.m, j.v, j.w, j.S, c,
+                                  sum, j.k);
+        else
+            hipExtLaunchKernelGGL((adamw_scalar_kernel<DT, Sum>), dim3(scalar), dim3(kThreads), 0,
+                                  stream, j.ev_start, j.ev_stop, 0, j.p, j.m, j.v, j.w, j.S, c,
+                                  sum, j.k);
+    } else if (j.out == nullptr) {
         if (j.aligned)
             hipLaunchKernelGGL((adamw_vec_kernel<DT, Sum, TP>), dim3(tiled), dim3(kThreads), 0,
                                stream, j.p, j.m, j.v, j.w, j.S, c, sum, j.k);
@@ -582,8 +597,9 @@ hipError_t dispatch(const Job& j, const PtrPack& c, int nd, int R, bool rnd, hip
 
 hipError_t launch_adamw(float* p, float* m, float* v, uint16_t* w, int64_t S,
                         const PtrPack& contribs, int nd, int R, bool rnd, int dtype,
-                        const AdamConsts& k, bool aligned, hipStream_t stream) {
-    const Job j{p, m, v, w, nullptr, S, k, aligned};
+                        const AdamConsts& k, bool aligned, hipStream_t stream,
+                        hipEvent_t ev_start, hipEvent_t ev_stop) {
+    const Job j{p, m, v, w, nullptr, S, k, aligned, ev_start, ev_stop};
     if (dtype == ZS_BF16) return dispatch<ZS_BF16>(j, contribs, nd, R, rnd, stream);
     return dispatch<ZS_F32>(j, contribs, nd, R, rnd, stream);
 }
@@ -592,7 +608,7 @@ hipError_t launch_reduce(const PtrPack& contribs, int nd, int R, bool rnd, int d
                          float inv_n, float* out, bool aligned, hipStream_t stream) {
     AdamConsts k{};
     k.inv_n = inv_n;
-    const Job j{nullptr, nullptr, nullptr, nullptr, out, S, k, aligned};
+    const Job j{nullptr, nullptr, nullptr, nullptr, out, S, k, aligned, nullptr, nullptr};
     if (dtype == ZS_BF16) return dispatch<ZS_BF16>(j, contribs, nd, R, rnd, stream);
     return dispatch<ZS_F32>(j, contribs, nd, R, rnd, stream);
 }

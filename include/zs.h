@@ -10,6 +10,8 @@
  *   zs_adamw_step    fused reduce + mixed-precision AdamW on one shard
  *   zs_reduce_shard_ex, zs_adamw_step_ex  the same under HYBRID_SHARD's
  *                    two-level reduce and/or reduce-dtype rounding
+ *   zs_adamw_step_timed  zs_adamw_step_ex with the kernel's own start and
+ *                    end recorded in two events (a measurement aid)
  *   zs_gather_unit   all-gather's local rebuild of a unit from its shards
  *   zs_step_pipelined  the step over a sequence of buckets, each bucket's
  *                    contribution transfer overlapped with the previous step
@@ -20,7 +22,7 @@
  *                    per-rank shard checkpoints, resumable at any D2
  *   zs_adamw_step_host, zs_offload_step
  *                    the step's AdamW on host cores (ZeRO-Offload)
- *   zs_stream_ceiling, zs_hbm_probe
+ *   zs_stream_ceiling, zs_stream_ceiling_timed, zs_hbm_probe
  *                    measurement aids: the step's memory streams without its
  *                    arithmetic, and HBM's rate for one direction alone
  *
@@ -277,6 +279,31 @@ zs_status zs_adamw_step_ex(float* p, float* m, float* v, uint16_t* w_out, int64_
                            int32_t dtype, const zs_adamw_hp* hp, hipStream_t stream);
 
 /*
+ * zs_adamw_step_timed -- zs_adamw_step_ex whose kernel carries two timing
+ * events: a measurement aid for benchmarks and profilers, same arithmetic,
+ * same results bit for bit.
+ *
+ * A step with S > 0 is exactly one kernel launch. This call makes it with
+ * hipExtLaunchKernel, which has the runtime record `start` at that kernel's
+ * start and `stop` at its end, with no marker packets enqueued around it, so
+ * hipEventElapsedTime(start, stop) times the kernel itself. (On MI355X, over
+ * the 70B shard's 0.7 ms launches, these events read 0.7% above a kernel
+ * trace's durations; events recorded with hipEventRecord before and after
+ * each launch read 0.9% above.)
+ *
+ *   start, stop  distinct events created by the caller on the current device
+ *                with timing enabled (hipEventCreate); each is re-recorded by
+ *                this call, as by hipEventRecord, and stays the caller's
+ * Other arguments and errors as zs_adamw_step_ex; ZS_EINVAL also when start
+ * or stop is NULL or they are the same event. With S == 0 nothing is
+ * launched and the events are not touched.
+ */
+zs_status zs_adamw_step_timed(float* p, float* m, float* v, uint16_t* w_out, int64_t S,
+                              const void* const* contribs, int32_t D, const zs_reduce_opts* opts,
+                              int32_t dtype, const zs_adamw_hp* hp, hipEvent_t start,
+                              hipEvent_t stop, hipStream_t stream);
+
+/*
  * zs_gather_unit -- the local data movement of all-gather.
  *
  * [GPT8] "AllGather vs AllReduce": afterwards every rank holds all blocks in
@@ -524,6 +551,19 @@ zs_status zs_offload_step(const void* const* contribs, int32_t D, int32_t dtype,
 zs_status zs_stream_ceiling(float* p, float* m, float* v, uint16_t* w, int64_t S,
                             const void* const* contribs, int32_t n, int32_t dtype,
                             hipStream_t stream);
+
+/*
+ * zs_stream_ceiling_timed -- zs_stream_ceiling whose one kernel launch records
+ * `start` and `stop` at its own start and end, as zs_adamw_step_timed does
+ * for the step, so that the two are timed alike.
+ *   start, stop  as zs_adamw_step_timed
+ * Errors: as zs_stream_ceiling; ZS_EINVAL also when start or stop is NULL or
+ * they are the same event. With S < 1024 nothing is launched and the events
+ * are not touched.
+ */
+zs_status zs_stream_ceiling_timed(float* p, float* m, float* v, uint16_t* w, int64_t S,
+                                  const void* const* contribs, int32_t n, int32_t dtype,
+                                  hipEvent_t start, hipEvent_t stop, hipStream_t stream);
 
 /*
  * zs_hbm_probe -- a measurement aid, not part of the step: the memory

@@ -36,10 +36,11 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("zs_unit_layout", "zs_pack_flat", "zs_reduce_shard", "zs_adamw_step",
               "zs_gather_unit", "zs_step_pipelined", "zs_reduce_shard_ex", "zs_adamw_step_ex",
-              "zs_step_pipelined_static",
+              "zs_adamw_step_timed", "zs_step_pipelined_static",
               "zs_reshard", "zs_shard_save", "zs_shard_info_read", "zs_shard_load",
               "zs_shard_load_resharded", "zs_adamw_step_host", "zs_offload_step",
-              "zs_stream_ceiling", "zs_hbm_probe", "zs_last_error", "zs_abi_version"):
+              "zs_stream_ceiling", "zs_stream_ceiling_timed", "zs_hbm_probe", "zs_last_error",
+              "zs_abi_version"):
         assert n in names
 
 
@@ -298,6 +299,27 @@ def test_hybrid_argument_errors(lib):
     arr[9] = cs[9]
     assert red(8, 0, 0) == zs.ZS_EINVAL
     assert red(4, 2, 1, out=None) == zs.ZS_EINVAL
+
+    # the timed step: both events required and distinct; its other checks
+    # are the _ex ones; S == 0 enqueues nothing and leaves the events alone
+    def timed(e0, e1, D=8, R=1, n=S):
+        o = B.zs_reduce_opts(R, 0)
+        return lib.zs_adamw_step_timed(p, m, v, w, n, arr, D, ctypes.byref(o), zs.ZS_BF16,
+                                       ctypes.byref(_hp()), e0, e1, None)
+
+    fake0, fake1 = ctypes.c_void_p(A + 0x7000), ctypes.c_void_p(A + 0x7100)
+    assert timed(None, fake1) == zs.ZS_EINVAL and "event" in zs.zs_last_error()
+    assert timed(fake0, None) == zs.ZS_EINVAL and "event" in zs.zs_last_error()
+    assert timed(fake0, fake0) == zs.ZS_EINVAL and "same event" in zs.zs_last_error()
+    assert timed(fake0, fake1, R=0) == zs.ZS_EINVAL and "replicas" in zs.zs_last_error()
+    assert timed(fake0, fake1, n=0) == zs.ZS_OK
+
+    def ceiling_timed(e0, e1, n=S):
+        return lib.zs_stream_ceiling_timed(p, m, v, w, n, arr, 8, zs.ZS_BF16, e0, e1, None)
+
+    assert ceiling_timed(None, fake1) == zs.ZS_EINVAL and "event" in zs.zs_last_error()
+    assert ceiling_timed(fake1, fake1) == zs.ZS_EINVAL and "same event" in zs.zs_last_error()
+    assert ceiling_timed(fake0, fake1, n=1023) == zs.ZS_OK
     assert red(4, 2, 1, out=cs[5] + 8) == zs.ZS_EALIAS
     assert lib.zs_reduce_shard_ex(arr, 8, None, zs.ZS_BF16, 0, None, None) == zs.ZS_OK
 
